@@ -1,0 +1,140 @@
+/*
+ * kvq.h - C ABI of the MI355X two-stage residual-VQ KV-cache codec (libkvq.so).
+ *
+ * The method (VeloxQuant-MLX blog, "rvq" tag page, "The pipeline, as it actually runs"):
+ * each head_dim vector of a [B, H, S, D] fp16 key or value tensor is normalised (its
+ * norm kept), rotated by a sign-flipped, normalised Walsh-Hadamard transform, quantized
+ * against a Gaussian Lloyd-Max codebook, its residual quantized against a Laplacian-fit
+ * codebook, and the two b-bit index streams are bit-packed into uint32 words, each
+ * stream separately. Decoding inverts every step except the quantization.
+ *
+ * Conventions shared by every entry point:
+ *   - No exceptions cross this boundary and nothing aborts: every call returns a
+ *     kvq_status. Argument checks run on the host before any HIP call, so a rejected
+ *     call touches no device state.
+ *   - The caller owns every buffer. The library allocates nothing, frees nothing and
+ *     keeps no global state; `cb` is only read during the call.
+ *   - Device calls enqueue on `stream` (a hipStream_t; NULL means the default stream)
+ *     and return without synchronising. A fault inside a kernel surfaces at the
+ *     caller's next synchronisation, not as a return code.
+ *   - Calls that overlap on one stream are ordered; on different streams they may run
+ *     concurrently and must not write the same words.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,    /* a required pointer is NULL, or a codebook struct is inconsistent */
+  KVQ_ERR_SHAPE = -2,  /* d not a power of two in [8, 1024]; bits not in 1..4; B, H, S < 0 */
+  KVQ_ERR_ALIGN = -3,  /* an fp16 or packed-word buffer not 16-byte aligned, or a norm buffer not 4-byte aligned */
+  KVQ_ERR_RANGE = -4,  /* s_offset < 0, s_offset + S > S_cap, or a size overflows 64 bits */
+  KVQ_ERR_DEVICE = -5  /* the HIP launch reported an error */
+} kvq_status;
+
+#define KVQ_MIN_D 8
+#define KVQ_MAX_D 1024
+#define KVQ_MAX_BITS 4
+
+/*
+ * Codebooks and rotation signs for one (d, bits) pair. Plain data, 416 bytes; build it
+ * with kvq_build_codebooks and treat it as read-only.
+ *
+ * c1/b1: stage-1 centroids (2^bits, ascending) and boundaries (2^bits - 1): the
+ *        Lloyd-Max quantizer of N(0, sigma1^2), sigma1^2 = 1/d (the variance of one
+ *        coordinate of a rotated unit vector).
+ * c2/b2: stage-2 tables: the Lloyd-Max quantizer of a zero-mean Laplace density whose
+ *        variance is the stage-1 distortion, sigma2^2 = mse_g * sigma1^2.
+ *        Boundaries are the float32-rounded midpoints of neighbouring centroids (blog,
+ *        "rvq" tag page, "What 'quantize' means here, precisely"); both tables are exactly
+ *        antisymmetric, so the middle boundary is +0.0.
+ * sign_bits: bit j (word j/32, bit j%32) set <=> the rotation multiplies coordinate j by -1.
+ */
+typedef struct kvq_codebooks {
+  int32_t d;               /* head dimension */
+  int32_t bits;            /* bits per code, per stage */
+  int32_t elems_per_word;  /* floor(32 / bits) codes in each uint32 word */
+  int32_t n_words;         /* ceil(d / elems_per_word) words per vector per stream */
+  float c1[16];
+  float b1[15];
+  float c2[16];
+  float b2[15];
+  double sigma1;           /* 1/sqrt(d) */
+  double sigma2;           /* sqrt(mse_g) * sigma1 */
+  double mse_g;            /* distortion of the unit-variance Gaussian Lloyd-Max quantizer */
+  uint32_t sign_bits[KVQ_MAX_D / 32];
+} kvq_codebooks;
+
+/*
+ * kvq_build_codebooks - host only, no device calls.
+ *   d     head dimension, a power of two in [8, 1024]
+ *   bits  bits per code per stage, 1..4
+ *   signs host array of d entries, each +1 or -1 (the rotation's sign vector), or NULL
+ *         for all +1
+ *   out   host struct to fill
+ * Lloyd-Max iteration in double precision for both densities (the pages: "rvq" tag page,
+ * "The pipeline, as it actually runs" names a Gaussian and a Laplacian-fit codebook;
+ * "turboquant" tag page, "Kernel 2" names Lloyd-Max; the "kivi" tag page's second post,
+ * "Where KIVI fits", calls RVQ's codebooks analytical, needing no calibration).
+ * Returns KVQ_ERR_ARG for a NULL out or a sign entry other than +-1, KVQ_ERR_SHAPE for
+ * d or bits out of range.
+ */
+kvq_status kvq_build_codebooks(int32_t d, int32_t bits, const int8_t* signs, kvq_codebooks* out);
+
+/*
+ * kvq_rvq_encode_pack - device. Encodes N = B*H*S vectors in one kernel launch.
+ *   cb        host pointer to codebooks from kvq_build_codebooks (read during the call)
+ *   x         device fp16 [B, H, S, d], contiguous, 16-byte aligned (raw IEEE half bits)
+ *   B, H, S   sizes (>= 0; any of them 0 means nothing to do)
+ *   packed1   device uint32 [B, H, S_cap, n_words], 16-byte aligned: stage-1 codes
+ *   packed2   device uint32 [B, H, S_cap, n_words], 16-byte aligned: stage-2 codes
+ *   norms     device float32 [B, H, S_cap], 4-byte aligned: ||x|| of each vector
+ *   S_cap     capacity of the cache's token axis (S_cap >= s_offset + S)
+ *   s_offset  token s of x is written at cache position s_offset + s (appending one
+ *             decode step at a time is S = 1, s_offset = step)
+ *   stream    hipStream_t or NULL
+ * Word layout (blog, "rvq" tag page, "The kernel"): code j of a vector goes to word
+ * j / elems_per_word at bits [(j % elems_per_word) * bits, ... + bits), LSB first; bits
+ * past the last code are 0. Code value = the number of boundaries the value exceeds
+ * ("What 'quantize' means here, precisely"), stage 1 on the rotated coordinate
+ * y = (H diag(s) x)_j / (sqrt(d) ||x||), stage 2 on the float32 residual y - c1[code1].
+ * A zero vector stores norm 0 and the codes of y = 0.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_SHAPE, KVQ_ERR_ALIGN, KVQ_ERR_RANGE (checked before any
+ * HIP call), KVQ_ERR_DEVICE (launch error). The packed outputs and x must not overlap.
+ */
+kvq_status kvq_rvq_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
+                               int64_t B, int64_t H, int64_t S,
+                               uint32_t* packed1, uint32_t* packed2, float* norms,
+                               int64_t S_cap, int64_t s_offset, void* stream);
+
+/*
+ * kvq_rvq_unpack_decode - device. Decodes cache positions [s_offset, s_offset + S) of
+ * every (b, h) in one launch.
+ *   packed1/packed2  device uint32 [B, H, S_cap, n_words] (layout as above)
+ *   norms            device float32 [B, H, S_cap], or NULL for unit-norm reconstructions
+ *   x_out            device fp16 [B, H, S, d], contiguous, 16-byte aligned
+ * Each coordinate is dequantized as c1[i1] + c2[i2] in the rotated domain (blog,
+ * "turboquant" tag page, "Kernel 5"), rotated back by diag(s) H / sqrt(d) (H is
+ * symmetric and H H = d I), scaled by the norm and rounded to fp16 (nearest-even).
+ * Errors as for kvq_rvq_encode_pack.
+ */
+kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb,
+                                 const uint32_t* packed1, const uint32_t* packed2,
+                                 const float* norms,
+                                 int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
+                                 uint16_t* x_out, void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* kvq_status_str(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

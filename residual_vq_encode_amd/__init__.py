@@ -1,0 +1,203 @@
+"""Python binding of libkvq, the MI355X two-stage residual-VQ KV-cache codec.
+
+Argument marshalling only: every step of the encode and decode runs in the HIP kernels
+of libkvq.so (built in place by ``python -m residual_vq_encode_amd.build``). PyTorch is
+used for device memory and streams; tensors are passed to the C ABI as raw pointers on
+the current torch stream. There is no fallback path: if the library is missing or the
+tensors are not on a GPU, the calls raise.
+
+    cb = build_codebooks(d=128, bits=2, signs=s)           # host, once
+    p1, p2, norms = encode(x, cb)                          # x: fp16 [B, H, S, D] on cuda
+    x_hat = decode(p1, p2, norms, cb)                      # fp16 [B, H, S, D]
+
+The lower-level calls kvq_rvq_encode_pack / kvq_rvq_unpack_decode mirror the C ABI
+(including S_cap / s_offset for writing into and reading from a preallocated cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "KvqError", "Codebooks", "load", "library_path", "build_codebooks", "kvq_build_codebooks",
+    "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str", "encode", "decode", "n_words",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libkvq.so"
+
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_SHAPE", -3: "KVQ_ERR_ALIGN",
+          -4: "KVQ_ERR_RANGE", -5: "KVQ_ERR_DEVICE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({kvq_status_str(status)})")
+
+
+class Codebooks(ctypes.Structure):
+    """Mirror of kvq_codebooks (include/kvq.h)."""
+    _fields_ = [
+        ("d", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("elems_per_word", ctypes.c_int32), ("n_words", ctypes.c_int32),
+        ("c1", ctypes.c_float * 16), ("b1", ctypes.c_float * 15),
+        ("c2", ctypes.c_float * 16), ("b2", ctypes.c_float * 15),
+        ("sigma1", ctypes.c_double), ("sigma2", ctypes.c_double), ("mse_g", ctypes.c_double),
+        ("sign_bits", ctypes.c_uint32 * 32),
+    ]
+
+    @property
+    def levels(self) -> int:
+        return 1 << self.bits
+
+    def tables(self):
+        """(c1, b1, c2, b2) as Python lists of the used entries."""
+        k = self.levels
+        return list(self.c1[:k]), list(self.b1[:k - 1]), list(self.c2[:k]), list(self.b2[:k - 1])
+
+    def signs(self) -> list[int]:
+        return [-1 if (self.sign_bits[j >> 5] >> (j & 31)) & 1 else 1 for j in range(self.d)]
+
+
+assert ctypes.sizeof(Codebooks) == 416
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load libkvq.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m residual_vq_encode_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, ptr = ctypes.c_int64, ctypes.c_void_p
+    lib.kvq_build_codebooks.argtypes = [ctypes.c_int32, ctypes.c_int32, ptr, ctypes.POINTER(Codebooks)]
+    lib.kvq_build_codebooks.restype = ctypes.c_int
+    lib.kvq_rvq_encode_pack.argtypes = [ctypes.POINTER(Codebooks), ptr, i64, i64, i64, ptr, ptr, ptr, i64, i64, ptr]
+    lib.kvq_rvq_encode_pack.restype = ctypes.c_int
+    lib.kvq_rvq_unpack_decode.argtypes = [ctypes.POINTER(Codebooks), ptr, ptr, ptr, i64, i64, i64, i64, i64, ptr, ptr]
+    lib.kvq_rvq_unpack_decode.restype = ctypes.c_int
+    lib.kvq_status_str.argtypes = [ctypes.c_int]
+    lib.kvq_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def kvq_status_str(status: int) -> str:
+    return load().kvq_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise KvqError(status, what)
+
+
+def n_words(d: int, bits: int) -> int:
+    epw = 32 // bits
+    return (d + epw - 1) // epw
+
+
+def kvq_build_codebooks(d: int, bits: int, signs=None) -> Codebooks:
+    """Host call. signs: None (all +1) or a sequence/array/tensor of d values in {+1, -1}."""
+    cb = Codebooks()
+    buf = None
+    if signs is not None:
+        vals = [int(v) for v in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+        if len(vals) != d:
+            raise ValueError(f"signs must have {d} entries")
+        buf = (ctypes.c_int8 * d)(*vals)
+    _check(load().kvq_build_codebooks(int(d), int(bits), buf, ctypes.byref(cb)), "kvq_build_codebooks")
+    return cb
+
+
+build_codebooks = kvq_build_codebooks
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _require_cuda(*tensors) -> None:
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("kvq kernels need GPU tensors (no CPU path exists)")
+
+
+def kvq_rvq_encode_pack(cb: Codebooks, x, packed1, packed2, norms, s_offset: int = 0, stream=None) -> None:
+    """x: fp16 [B, H, S, d] contiguous; packed1/packed2: int32/uint32 [B, H, S_cap, n_words];
+    norms: float32 [B, H, S_cap]. Writes token s of x at cache position s_offset + s."""
+    import torch
+    _require_cuda(x, packed1, packed2, norms)
+    if x.dtype != torch.float16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, d = x.shape
+    if d != cb.d:
+        raise ValueError(f"x has d={d}, codebooks have d={cb.d}")
+    S_cap = packed1.shape[2]
+    for name, t, shape in (("packed1", packed1, (B, H, S_cap, cb.n_words)),
+                           ("packed2", packed2, (B, H, S_cap, cb.n_words)),
+                           ("norms", norms, (B, H, S_cap))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape {shape}, got {tuple(t.shape)}")
+    if packed1.element_size() != 4 or packed2.element_size() != 4 or norms.dtype != torch.float32:
+        raise ValueError("packed streams must be 32-bit integers and norms float32")
+    _check(load().kvq_rvq_encode_pack(ctypes.byref(cb), _ptr(x), B, H, S, _ptr(packed1), _ptr(packed2),
+                                      _ptr(norms), S_cap, int(s_offset), _stream_handle(stream)),
+           "kvq_rvq_encode_pack")
+
+
+def kvq_rvq_unpack_decode(cb: Codebooks, packed1, packed2, norms, out, s_offset: int = 0, stream=None) -> None:
+    """Decodes cache positions [s_offset, s_offset + S) into out: fp16 [B, H, S, d].
+    norms=None gives unit reconstructions."""
+    import torch
+    _require_cuda(packed1, packed2, norms, out)
+    if out.dtype != torch.float16 or out.dim() != 4 or not out.is_contiguous() or out.shape[3] != cb.d:
+        raise ValueError("out must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, _ = out.shape
+    S_cap = packed1.shape[2]
+    for name, t, shape in (("packed1", packed1, (B, H, S_cap, cb.n_words)),
+                           ("packed2", packed2, (B, H, S_cap, cb.n_words))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with shape {shape}, got {tuple(t.shape)}")
+    if norms is not None and (tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32
+                              or not norms.is_contiguous()):
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    _check(load().kvq_rvq_unpack_decode(ctypes.byref(cb), _ptr(packed1), _ptr(packed2), _ptr(norms),
+                                        B, H, S_cap, int(s_offset), S, _ptr(out), _stream_handle(stream)),
+           "kvq_rvq_unpack_decode")
+
+
+def encode(x, cb: Codebooks, stream=None):
+    """Allocate outputs and encode x (fp16 [B, H, S, d] on cuda). Returns (packed1, packed2, norms)."""
+    import torch
+    B, H, S, d = x.shape
+    p1 = torch.empty((B, H, S, cb.n_words), dtype=torch.int32, device=x.device)
+    p2 = torch.empty_like(p1)
+    norms = torch.empty((B, H, S), dtype=torch.float32, device=x.device)
+    kvq_rvq_encode_pack(cb, x, p1, p2, norms, 0, stream)
+    return p1, p2, norms
+
+
+def decode(packed1, packed2, norms, cb: Codebooks, stream=None):
+    """Allocate the output and decode every cache position. Returns fp16 [B, H, S, d]."""
+    import torch
+    B, H, S, _ = packed1.shape
+    out = torch.empty((B, H, S, cb.d), dtype=torch.float16, device=packed1.device)
+    kvq_rvq_unpack_decode(cb, packed1, packed2, norms, out, 0, stream)
+    return out

@@ -1,0 +1,108 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI binding and judge
+it against the oracle with the comparison rule of oracle/flips.py.
+
+Inputs come from the seeded generator (synth) or are built by hand; the oracle always
+consumes the very bytes the device consumed, copied back to the host. Decoders are fed
+the oracle's packed words (uploaded), never words produced by the device.
+"""
+import numpy as np
+import torch
+
+import residual_vq_encode_amd as kvq
+from oracle import codebooks as ocb
+from oracle import flips, rvq
+
+# Tolerances. Codes: bit-exact except one-level flips of values within 1e-5 (relative, with
+# the stage scale as the floor at the boundary 0) of a boundary, at most 1e-6 of all
+# codes. Norms: the device sums squares of float16 inputs in float32 with 4 accumulators of
+# 16 pair-products each plus a 2-level tree, relative error <= 18 * 2^-24 on the square,
+# half that after the square root, plus one rounding: below 1e-6 relative.
+REL_WINDOW = 1e-5
+MAX_FLIP_FRACTION = 1e-6
+NORM_REL_TOL = 1e-6
+# Decode: on unit vectors (norms = NULL) the device and oracle reconstructions differ by
+# float32 butterfly rounding plus at most one float16 ulp (2^-11 for |x| < 1).
+DECODE_UNIT_ATOL = 1e-3
+
+_TABLES: dict = {}
+
+
+def _finite16(v: np.ndarray) -> np.ndarray:
+    """float16 values as float64 with +-inf replaced by +-65536, the power of two where
+    round-to-nearest-even overflows: a reconstruction that lands just past the float16 range
+    on one side and just inside it on the other then differs by one float16 step (32), as
+    it should, instead of producing inf - inf."""
+    v = v.astype(np.float64)
+    return np.where(np.isinf(v), np.sign(v) * 65536.0, v)
+
+
+def tables(d, bits):
+    if (d, bits) not in _TABLES:
+        _TABLES[(d, bits)] = ocb.build_tables(d, bits)
+    return _TABLES[(d, bits)]
+
+
+def as_u32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().numpy().view(np.uint32)
+
+
+def gpu_encode(x: torch.Tensor, signs, bits, S_cap=None, s_offset=0, fill=None):
+    """Encode fp16 [B, H, S, D] (cuda) into freshly allocated caches; returns cuda tensors."""
+    B, H, S, D = x.shape
+    S_cap = S if S_cap is None else S_cap
+    cb = kvq.build_codebooks(D, bits, signs)
+    p1 = torch.empty((B, H, S_cap, cb.n_words), dtype=torch.int32, device=x.device)
+    p2 = torch.empty_like(p1)
+    nrm = torch.empty((B, H, S_cap), dtype=torch.float32, device=x.device)
+    if fill is not None:
+        p1.fill_(fill), p2.fill_(fill), nrm.fill_(float("nan"))
+    kvq.kvq_rvq_encode_pack(cb, x, p1, p2, nrm, s_offset)
+    torch.cuda.synchronize()
+    return p1, p2, nrm
+
+
+def judge(x16_rows: np.ndarray, signs, bits, p1_rows: np.ndarray, p2_rows: np.ndarray, norm_rows: np.ndarray):
+    d = x16_rows.shape[1]
+    t = tables(d, bits)
+    ref = rvq.encode(x16_rows, np.asarray(signs, np.int8), t)
+    return flips.compare_encode(p1_rows, p2_rows, norm_rows, ref, t, REL_WINDOW), ref
+
+
+def check_encode(x: torch.Tensor, signs, bits, max_flip=MAX_FLIP_FRACTION):
+    """Encode x on the GPU and require the oracle's codes and norms under the rule."""
+    B, H, S, D = x.shape
+    p1, p2, nrm = gpu_encode(x, signs, bits)
+    x_rows = x.detach().cpu().numpy().reshape(-1, D)
+    rep, ref = judge(x_rows, signs, bits, as_u32(p1).reshape(-1, p1.shape[-1]),
+                     as_u32(p2).reshape(-1, p2.shape[-1]), nrm.cpu().numpy().reshape(-1))
+    assert rep.ok(max_flip, NORM_REL_TOL), rep.summary()
+    return rep, (p1, p2, nrm), ref
+
+
+def check_decode_from_oracle_words(ref: dict, signs, bits, shape, with_norms=True):
+    """Feed the oracle's packed words to the GPU decoder and to the oracle decoder."""
+    B, H, S, D = shape
+    t = tables(D, bits)
+    cb = kvq.build_codebooks(D, bits, signs)
+    dev = torch.device("cuda")
+    p1 = torch.from_numpy(ref["packed1"].view(np.int32)).reshape(B, H, S, -1).to(dev)
+    p2 = torch.from_numpy(ref["packed2"].view(np.int32)).reshape(B, H, S, -1).to(dev)
+    out = torch.empty((B, H, S, D), dtype=torch.float16, device=dev)
+    kvq.kvq_rvq_unpack_decode(cb, p1, p2, None, out)
+    torch.cuda.synchronize()
+    got = _finite16(out.cpu().numpy().reshape(-1, D))
+    want = _finite16(rvq.decode(ref["packed1"], ref["packed2"], None, np.asarray(signs), t))
+    err_unit = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err_unit <= DECODE_UNIT_ATOL, err_unit
+    err_rel = 0.0
+    if with_norms:
+        nrm = torch.from_numpy(ref["norms"]).reshape(B, H, S).to(dev)
+        kvq.kvq_rvq_unpack_decode(cb, p1, p2, nrm, out)
+        torch.cuda.synchronize()
+        got = _finite16(out.cpu().numpy().reshape(-1, D))
+        want = _finite16(rvq.decode(ref["packed1"], ref["packed2"], ref["norms"], np.asarray(signs), t))
+        scale = np.maximum(ref["norms"].astype(np.float64), 1e-30)[:, None]
+        err_rel = float(np.max(np.abs(got - want) / scale)) if got.size else 0.0
+        # relative to the vector's norm: the unit-case bound plus float16 rounding of the product
+        assert err_rel <= DECODE_UNIT_ATOL, err_rel
+    return err_unit, err_rel

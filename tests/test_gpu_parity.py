@@ -1,0 +1,259 @@
+"""GPU parity: the HIP encode/decode through the C ABI against the CPU oracle.
+
+Codes must equal the oracle's bit for bit except for one-level flips of values within the
+boundary window (at most 1e-6 of all codes); norms within 1e-6 relative; decoders fed the
+same packed words agree within 1e-3 on unit vectors. Workload shapes are the five
+synthetic workloads plus the pages' parity grid (VeloxQuant-MLX blog, "rvq" tag page,
+"Bit-exactness, checked the boring way": D in 8..256, bits 1..4, N in {1, 5, 33}), ragged
+tails, degenerate inputs, cache-window writes and determinism.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import residual_vq_encode_amd as kvq
+import synth
+from oracle import rvq
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+D_ONE_LANE = [8, 16, 32, 64, 128]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _signs(seed, d):
+    return synth.signs(seed, d).numpy()
+
+
+# ------------------------------------------------------------------------- worked examples
+
+def test_worked_examples_on_gpu():
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))["cases"]
+    for c in cases:
+        _say(f"worked example {c['name']}")
+        x = torch.tensor([[[c["x"]]]], dtype=torch.float16, device=DEV)
+        p1, p2, nrm = gu.gpu_encode(x, c["signs"], c["bits"])
+        assert gu.as_u32(p1).ravel().tolist() == c["packed1"], c["name"]
+        assert gu.as_u32(p2).ravel().tolist() == c["packed2"], c["name"]
+        assert float(nrm.item()) == c["norm"]
+
+
+# ------------------------------------------------------------------------- pages' grid
+
+@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 5, 33])
+def test_parity_grid(d, bits, n):
+    _say(f"grid d={d} bits={bits} n={n}")
+    spec = synth.TensorSpec(1, 1, n, d, "gauss", d + bits + n)
+    x = synth.tensor(spec, device=DEV)
+    gu.check_encode(x, _signs(1000 + d, d), bits)
+
+
+@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_decode_grid(d, bits):
+    _say(f"decode d={d} bits={bits}")
+    spec = synth.TensorSpec(2, 3, 37, d, "gauss", 77 + d + bits)
+    x = synth.rows(spec).numpy().reshape(-1, d)
+    s = _signs(2000 + d, d)
+    ref = rvq.encode(x, s, gu.tables(d, bits))
+    gu.check_decode_from_oracle_words(ref, s, bits, (2, 3, 37, d))
+
+
+# ------------------------------------------------------------------------- tiles and tails
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [63, 64, 65, 127, 129, 1000, 4097, 70001])
+def test_ragged_tiles(bits, n):
+    _say(f"ragged bits={bits} n={n}")
+    spec = synth.TensorSpec(1, 1, n, 128, "gauss_outliers", 31 + n)
+    gu.check_encode(synth.tensor(spec, device=DEV), _signs(5, 128), bits)
+
+
+# ------------------------------------------------------------------------- workloads
+
+def test_workload_tiny():
+    w = synth.WORKLOADS["tiny"]
+    _say("workload tiny [1,2,64,128] b=2 signs +1")
+    x = synth.tensor(w.tensors[0], device=DEV)
+    rep, _, ref = gu.check_encode(x, np.ones(128, np.int8), 2)
+    assert rep.flips == 0
+    gu.check_decode_from_oracle_words(ref, np.ones(128, np.int8), 2, tuple(x.shape))
+
+
+def test_workload_llama_layer():
+    w = synth.WORKLOADS["llama_layer"]
+    _say("workload llama_layer [1,32,8192,128] b=2")
+    x = synth.tensor(w.tensors[0], device=DEV)
+    s = _signs(w.sign_seed, 128)
+    rep, (p1, p2, nrm), ref = gu.check_encode(x, s, 2)
+    _say(rep.summary())
+    gu.check_decode_from_oracle_words(ref, s, 2, tuple(x.shape))
+    # round trip on the device: reconstructions of the device's own codes
+    cb = kvq.build_codebooks(128, 2, s)
+    xr = kvq.decode(p1, p2, nrm, cb).float()
+    cos = torch.nn.functional.cosine_similarity(xr.reshape(-1, 128), x.float().reshape(-1, 128), dim=1)
+    assert float(cos.mean()) > 0.97 and float(cos.min()) > 0.85
+
+
+@pytest.mark.parametrize("bits", [1, 4])
+def test_workload_gqa_long(bits):
+    w = synth.WORKLOADS["gqa_long"]
+    _say(f"workload gqa_long [1,8,32768,128] b={bits}")
+    x = synth.tensor(w.tensors[0], device=DEV)
+    rep, _, _ = gu.check_encode(x, _signs(w.sign_seed, 128), bits)
+    _say(rep.summary())
+
+
+def test_workload_prefill_kv_sampled():
+    """Full-size keys and values [16,32,4096,128] at b=4, encoded in the full launch; the
+    oracle checks 32768 sampled vectors of each, and every norm is checked against a
+    float64 reduction on the device."""
+    w = synth.WORKLOADS["prefill_kv"]
+    s = _signs(w.sign_seed, 128)
+    g = torch.Generator().manual_seed(4)
+    for spec in w.tensors:
+        _say(f"workload prefill_kv seed={spec.seed} [16,32,4096,128] b=4")
+        x = synth.tensor(spec, device=DEV)
+        p1, p2, nrm = gu.gpu_encode(x, s, 4)
+        n64 = torch.linalg.vector_norm(x.double().reshape(-1, 128), dim=1)
+        rel = ((nrm.double().reshape(-1) - n64).abs() / n64).max().item()
+        assert rel <= gu.NORM_REL_TOL, rel
+        idx = torch.randperm(spec.rows, generator=g)[:32768].sort().values
+        rows = x.reshape(-1, 128)[idx.to(DEV)].cpu().numpy()
+        rep, _ = gu.judge(rows, s, 4, gu.as_u32(p1.reshape(-1, 16)[idx.to(DEV)]),
+                          gu.as_u32(p2.reshape(-1, 16)[idx.to(DEV)]), nrm.reshape(-1)[idx.to(DEV)].cpu().numpy())
+        _say(rep.summary())
+        assert rep.ok(gu.MAX_FLIP_FRACTION, gu.NORM_REL_TOL), rep.summary()
+        del x, p1, p2, nrm
+
+
+def test_workload_decode_append():
+    """2000 decode steps, each one token for [256, 8] heads written at s_offset = step of
+    caches with S_cap = 32768; sampled steps against the oracle, untouched tail intact."""
+    w = synth.WORKLOADS["decode_append"]
+    spec = w.tensors[0]
+    B, H, D, S_cap = spec.B, spec.H, spec.D, synth.DECODE_APPEND_S_CAP
+    s = _signs(w.sign_seed, D)
+    cb = kvq.build_codebooks(D, 2, s)
+    p1 = torch.full((B, H, S_cap, cb.n_words), -1, dtype=torch.int32, device=DEV)
+    p2 = torch.full_like(p1, -1)
+    nrm = torch.full((B, H, S_cap), float("nan"), dtype=torch.float32, device=DEV)
+    steps = [synth.step_rows(spec, t, device=DEV) for t in range(spec.S)]
+    _say("workload decode_append: 2000 launches")
+    for t, xt in enumerate(steps):
+        kvq.kvq_rvq_encode_pack(cb, xt, p1, p2, nrm, s_offset=t)
+    torch.cuda.synchronize()
+    for t in (0, 1, 63, 64, 999, 1999):
+        rows = steps[t].reshape(-1, D).cpu().numpy()
+        rep, _ = gu.judge(rows, s, 2, gu.as_u32(p1[:, :, t]).reshape(-1, 8), gu.as_u32(p2[:, :, t]).reshape(-1, 8),
+                          nrm[:, :, t].cpu().numpy().reshape(-1))
+        assert rep.ok(gu.MAX_FLIP_FRACTION, gu.NORM_REL_TOL), (t, rep.summary())
+    assert bool((p1[:, :, spec.S:] == -1).all()) and bool((p2[:, :, spec.S:] == -1).all())
+    assert bool(torch.isnan(nrm[:, :, spec.S:]).all())
+
+
+# ------------------------------------------------------------------------- degenerate inputs
+
+def _degenerate_rows(d):
+    rows = [np.zeros(d), np.ones(d), -np.ones(d), np.full(d, 65504.0), np.full(d, 2.0 ** -24)]
+    for j in (0, 1, d // 2, d - 1):
+        e = np.zeros(d)
+        e[j] = 3.0
+        rows.append(e)
+        rows.append(-e)
+    two = np.zeros(d)
+    two[0], two[1] = 1.0, 1.0
+    rows.append(two)
+    alt = np.where(np.arange(d) % 2 == 0, 1.0, -1.0)
+    rows.append(alt)
+    rows.append(np.where(np.arange(d) < d // 2, 0.5, -0.25))
+    neg0 = np.zeros(d)
+    rows.append(-neg0 * 0.0 - 0.0)  # all -0.0
+    rng = np.random.default_rng(9)
+    rows.append(rng.standard_normal(d) * 1e-4)  # mixes subnormal and normal float16
+    return np.stack(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("sign_kind", ["plus", "random"])
+def test_degenerate_inputs(d, bits, sign_kind):
+    """Zero vectors, constants, one-hot and two-hot vectors, the largest and smallest
+    float16, negative zeros: exact zeros appear in the rotated vector and must take the
+    count semantics (0 is not above the middle boundary)."""
+    _say(f"degenerate d={d} bits={bits} signs={sign_kind}")
+    rows = _degenerate_rows(d)
+    s = np.ones(d, np.int8) if sign_kind == "plus" else _signs(77, d)
+    x = torch.from_numpy(rows).to(DEV).reshape(1, 1, -1, d)
+    rep, _, ref = gu.check_encode(x, s, bits, max_flip=0.0)
+    gu.check_decode_from_oracle_words(ref, s, bits, tuple(x.shape))
+
+
+# ------------------------------------------------------------------------- cache windows
+
+@pytest.mark.parametrize("S,S_cap,s_offset", [(1, 7, 3), (5, 9, 4), (64, 200, 100), (100, 100, 0), (130, 300, 1)])
+def test_cache_window(S, S_cap, s_offset):
+    _say(f"cache window S={S} S_cap={S_cap} s_offset={s_offset}")
+    spec = synth.TensorSpec(3, 2, S, 128, "gauss", 55 + S)
+    x = synth.tensor(spec, device=DEV)
+    s = _signs(56, 128)
+    p1, p2, nrm = gu.gpu_encode(x, s, 2, S_cap=S_cap, s_offset=s_offset, fill=-1)
+    win = slice(s_offset, s_offset + S)
+    rep, ref = gu.judge(x.cpu().numpy().reshape(-1, 128), s, 2, gu.as_u32(p1[:, :, win]).reshape(-1, 8),
+                        gu.as_u32(p2[:, :, win]).reshape(-1, 8), nrm[:, :, win].cpu().numpy().reshape(-1))
+    assert rep.ok(gu.MAX_FLIP_FRACTION, gu.NORM_REL_TOL), rep.summary()
+    outside = torch.ones(S_cap, dtype=torch.bool)
+    outside[win] = False
+    assert bool((p1[:, :, outside] == -1).all()) and bool((p2[:, :, outside] == -1).all())
+    assert bool(torch.isnan(nrm[:, :, outside]).all())
+    # decode the window back (oracle words uploaded into a cache of the same geometry)
+    cb = kvq.build_codebooks(128, 2, s)
+    c1 = torch.zeros_like(p1)
+    c2 = torch.zeros_like(p2)
+    c1[:, :, win] = torch.from_numpy(ref["packed1"].view(np.int32)).reshape(3, 2, S, 8).to(DEV)
+    c2[:, :, win] = torch.from_numpy(ref["packed2"].view(np.int32)).reshape(3, 2, S, 8).to(DEV)
+    out = torch.empty((3, 2, S, 128), dtype=torch.float16, device=DEV)
+    kvq.kvq_rvq_unpack_decode(cb, c1, c2, None, out, s_offset=s_offset)
+    torch.cuda.synchronize()
+    want = rvq.decode(ref["packed1"], ref["packed2"], None, s, gu.tables(128, 2)).astype(np.float64)
+    assert np.max(np.abs(out.cpu().numpy().reshape(-1, 128).astype(np.float64) - want)) <= gu.DECODE_UNIT_ATOL
+
+
+# ------------------------------------------------------------------------- misc
+
+def test_empty_and_determinism():
+    cb = kvq.build_codebooks(128, 2)
+    x = torch.empty((0, 32, 16, 128), dtype=torch.float16, device=DEV)
+    p1, p2, nrm = kvq.encode(x, cb)
+    assert p1.numel() == 0
+    spec = synth.TensorSpec(1, 4, 4096, 128, "gauss", 3)
+    x = synth.tensor(spec, device=DEV)
+    s = _signs(8, 128)
+    a = gu.gpu_encode(x, s, 2)
+    b = gu.gpu_encode(x, s, 2)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_misaligned_device_pointer_rejected():
+    cb = kvq.build_codebooks(128, 2)
+    buf = torch.zeros(4 * 128 + 8, dtype=torch.float16, device=DEV)
+    x = buf[8:].view(1, 1, 4, 128)  # 16-byte aligned
+    xm = buf[1:1 + 512].view(1, 1, 4, 128)  # 2-byte offset
+    p1 = torch.empty((1, 1, 4, 8), dtype=torch.int32, device=DEV)
+    p2 = torch.empty_like(p1)
+    nrm = torch.empty((1, 1, 4), dtype=torch.float32, device=DEV)
+    kvq.kvq_rvq_encode_pack(cb, x, p1, p2, nrm)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_rvq_encode_pack(cb, xm, p1, p2, nrm)
+    assert e.value.status == -3
+    torch.cuda.synchronize()

@@ -1,0 +1,134 @@
+"""The C ABI library on the host: exports, struct layout, codebooks, argument checks.
+
+Nothing here launches a kernel: every call either is host-only (kvq_build_codebooks,
+kvq_status_str) or is rejected by the host-side argument checks before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import residual_vq_encode_amd as kvq
+from oracle import codebooks as ocb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.load()
+    names = _declared_functions()
+    assert names == ["kvq_build_codebooks", "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(kvq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    """Compile the header with gcc and compare sizeof/offsetof with the ctypes mirror."""
+    fields = [f for f, _ in kvq.Codebooks._fields_]
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"kvq.h\"\nint main(void){printf(\"%zu\", sizeof(kvq_codebooks));"
+    for f in fields:
+        src += f'printf(" %zu", offsetof(kvq_codebooks, {f}));'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "probe.c")
+        exe = os.path.join(td, "probe")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(kvq.Codebooks) == 416
+    assert vals[1:] == [getattr(kvq.Codebooks, f).offset for f in fields]
+
+
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebooks_match_oracle_bit_exactly(d, bits):
+    """The library's C++ Lloyd-Max builder and the oracle's numpy one are independent
+    implementations of the same fixed point; the float32 tables must agree exactly."""
+    rng = np.random.default_rng(d * 10 + bits)
+    signs = np.where(rng.integers(0, 2, d) == 1, -1, 1)
+    cb = kvq.build_codebooks(d, bits, signs)
+    t = ocb.build_tables(d, bits)
+    c1, b1, c2, b2 = (np.array(v, np.float32) for v in cb.tables())
+    assert c1.tobytes() == t.c1.tobytes() and b1.tobytes() == t.b1.tobytes()
+    assert c2.tobytes() == t.c2.tobytes() and b2.tobytes() == t.b2.tobytes()
+    assert cb.d == d and cb.bits == bits and cb.elems_per_word == 32 // bits
+    assert cb.n_words == -(-d // (32 // bits))
+    assert cb.signs() == signs.tolist()
+    assert abs(cb.sigma1 - t.sigma1) < 1e-15 and abs(cb.sigma2 / t.sigma2 - 1) < 1e-12
+
+
+def test_build_codebooks_rejects():
+    lib = kvq.load()
+    cb = kvq.Codebooks()
+    for d in (0, 4, 12, 2048, -8):
+        assert lib.kvq_build_codebooks(d, 2, None, ctypes.byref(cb)) == -2
+    for b in (0, 5, -1):
+        assert lib.kvq_build_codebooks(128, b, None, ctypes.byref(cb)) == -2
+    assert lib.kvq_build_codebooks(128, 2, None, None) == -1
+    bad = (ctypes.c_int8 * 8)(1, 1, 0, 1, 1, 1, 1, 1)
+    assert lib.kvq_build_codebooks(8, 2, bad, ctypes.byref(cb)) == -1
+    assert kvq.kvq_status_str(-3).startswith("misaligned") and kvq.kvq_status_str(99) == "unknown status"
+
+
+def _enc(cb, x, B, H, S, p1, p2, nrm, S_cap, s_off):
+    lib = kvq.load()
+    return lib.kvq_rvq_encode_pack(cb, x, B, H, S, p1, p2, nrm, S_cap, s_off, None)
+
+
+def _dec(cb, p1, p2, nrm, B, H, S_cap, s_off, S, out):
+    lib = kvq.load()
+    return lib.kvq_rvq_unpack_decode(cb, p1, p2, nrm, B, H, S_cap, s_off, S, out, None)
+
+
+def test_host_side_argument_checks():
+    """Every rejection below happens before any HIP call (fake pointers are never used)."""
+    cb = kvq.build_codebooks(128, 2)
+    pcb = ctypes.byref(cb)
+    A = 0x10000  # a 16-byte aligned fake address: only reached by calls that must reject
+    # null codebooks / inconsistent codebooks
+    assert _enc(None, A, 1, 1, 1, A, A, A, 1, 0) == -1
+    broken = kvq.Codebooks.from_buffer_copy(cb)
+    broken.n_words = 7
+    assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -1
+    broken = kvq.Codebooks.from_buffer_copy(cb)
+    broken.d = 96
+    assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -2
+    # shapes and ranges
+    assert _enc(pcb, A, -1, 1, 1, A, A, A, 1, 0) == -2
+    assert _enc(pcb, A, 1, 1, 5, A, A, A, 4, 0) == -4        # S > S_cap
+    assert _enc(pcb, A, 1, 1, 2, A, A, A, 4, 3) == -4        # s_offset + S > S_cap
+    assert _enc(pcb, A, 1, 1, 1, A, A, A, 4, -1) == -4
+    assert _enc(pcb, A, 1 << 40, 1 << 20, 1, A, A, A, 1, 0) == -4   # overflow
+    # nothing to do: OK without touching any pointer
+    assert _enc(pcb, None, 0, 32, 8, None, None, None, 8, 0) == 0
+    assert _dec(pcb, None, None, None, 4, 0, 8, 0, 8, None) == 0
+    # null and misaligned buffers
+    assert _enc(pcb, None, 1, 1, 1, A, A, A, 1, 0) == -1
+    assert _enc(pcb, A, 1, 1, 1, A, None, A, 1, 0) == -1
+    assert _enc(pcb, A + 8, 1, 1, 1, A, A, A, 1, 0) == -3
+    assert _enc(pcb, A, 1, 1, 1, A + 4, A, A, 1, 0) == -3
+    assert _enc(pcb, A, 1, 1, 1, A, A, A + 2, 1, 0) == -3
+    assert _dec(pcb, A, A, None, 1, 1, 4, 0, 4, A + 2) == -3
+    assert _dec(pcb, None, A, None, 1, 1, 4, 0, 4, A) == -1
+    assert _dec(pcb, A, A, None, 1, 1, 4, 2, 4, A) == -4
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    cb = kvq.build_codebooks(128, 2)
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        kvq.encode(x, cb)
