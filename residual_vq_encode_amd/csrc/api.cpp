@@ -20,8 +20,10 @@ using kvq::DecodeArgs;
 using kvq::EncodeArgs;
 using kvq::RowMap;
 
-// Persistent grid: enough 256-thread blocks to fill every CU a few times over; each wave
-// walks tiles of 64 vectors with a grid stride.
+// Persistent grid: two 256-thread blocks per compute unit (the LDS tile buffers and the
+// register budget allow two resident blocks per CU; MI355X has 256 CUs), so every wave is
+// resident from the start and walks tiles of 64 vectors with a grid stride, loading its
+// next tile while it computes the current one.
 constexpr int kMaxBlocks = 2048;
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -120,20 +122,19 @@ float as_float(int32_t v) {
 
 kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
   const int d = cb->d, bits = cb->bits, k = 1 << bits, half = k / 2;
-  const double s0 = sign_of(cb, 0);
   const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
-  std::memset(&a->sg, 0, sizeof(a->sg));
+  std::memset(a->xmask, 0, sizeof(a->xmask));
   std::memset(a->tab1, 0, sizeof(a->tab1));
   std::memset(a->tab2, 0, sizeof(a->tab2));
   a->j1max = a->j2max = 0;
   a->cm2[0] = a->cm2[1] = 0.f;
   if (bits == 1) {
-    a->k_scale = static_cast<float>(s0 * inv_sqrt_d);  // NX = -y_true
+    a->k_scale = static_cast<float>(inv_sqrt_d);  // NX = -y_true
     a->r12 = 1.f;
     a->cm2[0] = cb->c1[1];
   } else if (bits == 2) {
     const double T1 = cb->b1[2], T2 = cb->b2[2];
-    a->k_scale = static_cast<float>(s0 * (2.0 / T1) * inv_sqrt_d);
+    a->k_scale = static_cast<float>((2.0 / T1) * inv_sqrt_d);
     a->r12 = static_cast<float>(T1 / T2);
     a->cm2[0] = static_cast<float>(cb->c1[2] * (2.0 / T2));
     a->cm2[1] = static_cast<float>(cb->c1[3] * (2.0 / T2));
@@ -141,7 +142,7 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
     Buckets b1, b2;
     if (!make_buckets(cb->b1, bits, &b1, kvq::kTab1Max) || !make_buckets(cb->b2, bits, &b2, kvq::kTab2Max))
       return KVQ_ERR_ARG;
-    a->k_scale = static_cast<float>(s0 * b1.unit * inv_sqrt_d);
+    a->k_scale = static_cast<float>(b1.unit * inv_sqrt_d);
     a->r12 = static_cast<float>(b2.unit / b1.unit);
     a->j1max = b1.jmax;
     a->j2max = b2.jmax;
@@ -158,27 +159,8 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
       a->tab2[j][1] = as_float(b2.mbase[j]);
     }
   }
-  if (d <= 128) {
-    // sign-carried butterfly multipliers: merging blocks P = [q, q+h) and Q = [q+h, q+2h)
-    // multiplies Q by s_q * s_(q+h) (each block carries the sign of its first coordinate)
-    const int G = d < 16 ? d : 16;
-    auto mult = [&](int q, int h) { return static_cast<float>(sign_of(cb, q) * sign_of(cb, q + h)); };
-    for (int g = 0; g < d / G; ++g) {
-      int off = g * G;
-      for (int h = 1; h < G; h <<= 1) {
-        for (int p = 0; p < G / (2 * h); ++p) a->sg.t[off + p] = mult(g * G + 2 * h * p, h);
-        off += G / (2 * h);
-      }
-    }
-    int off = d;
-    for (int h = G; h < d; h <<= 1) {
-      for (int p = 0; p < d / (2 * h); ++p) a->sg.t[off + p] = mult(2 * h * p, h);
-      off += d / (2 * h);
-    }
-  } else {
-    for (int m = 0; m < d / 2; ++m)
-      a->sg.xmask[m] = (sign_of(cb, 2 * m) < 0 ? 0x8000u : 0u) | (sign_of(cb, 2 * m + 1) < 0 ? 0x80000000u : 0u);
-  }
+  for (int m = 0; m < d / 2; ++m)
+    a->xmask[m] = (sign_of(cb, 2 * m) < 0 ? 0x8000u : 0u) | (sign_of(cb, 2 * m + 1) < 0 ? 0x80000000u : 0u);
   return KVQ_OK;
 }
 

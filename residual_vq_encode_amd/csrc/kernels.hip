@@ -12,16 +12,17 @@
 // The pages' Metal kernel runs one threadgroup per vector and one thread per coordinate,
 // stages codes in threadgroup memory and packs them after a barrier. Here each lane of a
 // 64-wide wavefront owns a whole vector (D <= 128 coordinates in registers):
-//  * a wave loads 64 consecutive vectors with fully coalesced 16-byte loads and
-//    transposes them through a per-wave LDS buffer whose 16-byte chunks are XOR-swizzled
-//    so both the row-wise writes and the lane-per-row reads are bank-conflict free;
+//  * a wave streams 64 consecutive vectors (one tile) straight from HBM into its own LDS
+//    buffer with coalesced 16-byte direct-to-LDS loads (global_load_lds_dwordx4), then each
+//    lane reads its row back; the 16-byte chunks are XOR-swizzled so the lane-per-row reads
+//    are bank-conflict free. The next tile's loads are issued as soon as the current tile
+//    has left LDS, so they fly while the current tile is computed (software pipelining
+//    without spending registers on the prefetch);
 //  * the Walsh-Hadamard transform runs entirely in registers (log2 D butterfly stages, no
-//    cross-lane traffic, no barriers). The sign flip diag(s) costs nothing: a block of
-//    2^k coordinates is carried with the sign of its first input coordinate factored out,
-//    so merging blocks P and Q is (P + t Q, P - t Q) with t = s_start(P) * s_start(Q), one
-//    FMA per output with a wave-uniform +-1 multiplier, and the first stage reads the fp16
-//    inputs directly (v_fma_mix). The whole transform carries the factor s_0, folded into
-//    the per-vector scale;
+//    cross-lane traffic, no barriers). The sign flip diag(s) is an exact XOR of the fp16
+//    sign bits with per-pair masks read from a small LDS table (every lane reads the same
+//    address, a broadcast); the first stage reads the flipped fp16 pairs directly
+//    (v_dot2 with (1, 1) and (1, -1): one instruction per output, exact products);
 //  * quantization is branch-free; codes are shifted into their words with v_alignbit /
 //    shift-or as they are produced, so no code ever leaves registers.
 // No MFMA: the transform is O(D log D) additions with +-1 coefficients, and the kernel is
@@ -29,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <utility>
 
 #include "params.h"
 
@@ -54,20 +56,62 @@ __device__ __forceinline__ int swz(int row) {
 // executed in order, so only the compiler needs to be kept from moving accesses across.
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-// The sign multipliers inside the kernel's only argument (an EncodeArgs at offset 0 of the
-// kernel-argument segment), addressed without taking the argument's address (which would
-// force a private copy of the whole struct). Loads through this constant-address-space
-// pointer with uniform offsets are scalar (s_load), costing no vector instructions.
-typedef __attribute__((address_space(4))) const float* kargf_t;
-__device__ __forceinline__ kargf_t karg_multipliers() {
-  const __attribute__((address_space(4))) char* base =
-      (const __attribute__((address_space(4))) char*)(__builtin_amdgcn_kernarg_segment_ptr());
-  return reinterpret_cast<kargf_t>(base + offsetof(EncodeArgs, sg));
+// Explicit waits: every vector-memory operation of this wave has completed (the tile's
+// direct-to-LDS loads have landed), and every LDS read and scalar load of this wave has
+// returned (the tile buffer may be overwritten; asm-issued scalar loads are usable).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// fp16x2 dot product with a float32 addend, the non-accumulating (VOP3P) form: the
+// compiler otherwise picks the accumulating v_dot2c and spends a move zeroing each
+// destination. `w` holds two fp16 weights (low half weighs the pair's first element).
+constexpr uint32_t kPP = 0x3C003C00u;  // (+1, +1)
+constexpr uint32_t kPM = 0xBC003C00u;  // (+1, -1)
+constexpr uint32_t kMM = 0xBC00BC00u;  // (-1, -1)
+constexpr uint32_t kMP = 0x3C00BC00u;  // (-1, +1)
+__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w, float addend, bool zero_addend) {
+  float r;
+  if (zero_addend) {
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(pair), "s"(w));
+  } else {
+    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "s"(w), "v"(addend));
+  }
+  return r;
+}
+
+// Issues the direct-to-LDS loads of one tile: instruction k writes LDS slots
+// [64k, 64k + 64) (lane i -> slot 64k + i), and slot s = r*CH + c' of row r receives
+// the row's global chunk c' ^ swz(r). Rows at or past nv (the last, partial tile) re-read
+// row nv - 1, so every load stays inside the input; those lanes' results are never stored.
+template <int CH>
+__device__ __forceinline__ void dma_tile(uint4* buf, const uint4* src, int nv, int lane) {
+  const char* base = reinterpret_cast<const char*>(src);  // wave-uniform
+  if (nv == 64) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int slot = k * 64 + lane, r = slot / CH, c = (slot % CH) ^ swz<CH>(r);
+      const uint32_t off = static_cast<uint32_t>(r * CH + c) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int slot = k * 64 + lane, r = slot / CH, c = (slot % CH) ^ swz<CH>(r);
+      const int rr = r < nv ? r : nv - 1;
+      const uint32_t off = static_cast<uint32_t>(rr * CH + c) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, 0);
+    }
+  }
 }
 
 // Cache row of flattened input vector v0 + lane: (v / S) * S_cap + s_offset + v % S.
+// CONTIG (S == S_cap, s_offset == 0, chosen on the host) compiles to v0 + lane.
+template <bool CONTIG>
 __device__ __forceinline__ int64_t cache_row(const RowMap& m, int64_t v0, int lane) {
-  if (m.contiguous) return v0 + lane;
+  if constexpr (CONTIG) return v0 + lane;
   const int64_t q0 = v0 / m.S;          // once per tile (wave-uniform)
   const int64_t s0 = v0 - q0 * m.S;
   int64_t t = s0 + lane;                // < S + 64
@@ -129,8 +173,8 @@ constexpr uint32_t field_ones(int cnt) {  // bit 0 of every field
 
 // ------------------------------------------------------------------------------ encode
 
-template <int D, int BITS>
-__global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
+template <int D, int BITS, bool CONTIG>
+__global__ __launch_bounds__(kBlockThreads, 2) void encode_l1(const EncodeArgs a) {
   static_assert(D >= 8 && D <= 128 && (D & (D - 1)) == 0, "one vector per lane needs D <= 128");
   constexpr int CH = D / 8;                 // 16-byte chunks per vector
   constexpr int EPW = 32 / BITS;            // codes per word
@@ -138,49 +182,59 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
   constexpr int HALFM1 = (1 << (BITS - 1)) - 1;
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
+  __shared__ uint4 smask[CH];  // per-pair fp16 sign masks, 8 pairs per 16 bytes
   __shared__ float4 t1s[kTab1Max];
   __shared__ float2 t2s[kTab2Max];
+  for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   if constexpr (BITS >= 3) {
     for (int i = threadIdx.x; i < kTab1Max; i += kBlockThreads)
       t1s[i] = make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3]);
     for (int i = threadIdx.x; i < kTab2Max; i += kBlockThreads) t2s[i] = make_float2(a.tab2[i][0], a.tab2[i][1]);
-    __syncthreads();
   }
+  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   uint4* buf = stage[wv];
-  const int64_t n_tiles = (a.n_vec + 63) >> 6;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  // tile indices fit in 32 bits: 2^31 tiles of 64 vectors of >= 16 bytes exceed any HBM
+  const int n_tiles = static_cast<int>((a.n_vec + 63) >> 6);
+  const int stride = static_cast<int>(gridDim.x) * kWavesPerBlock;
+  const uint4* x16 = reinterpret_cast<const uint4*>(a.x);
+  // this lane's row inside the tile buffer: chunk c sits at slot (lane*CH + c) ^ swz(lane),
+  // i.e. at `rbase ^ c` since the swizzle only touches the low log2(CH) bits
+  const int rbase0 = lane * CH + swz<CH>(lane);
 
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wv; tile < n_tiles; tile += stride) {
-    const int64_t v0 = tile << 6;
+  int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
+  if (tile < n_tiles) {
+    const int64_t v0 = static_cast<int64_t>(tile) << 6;
+    dma_tile<CH>(buf, x16 + v0 * CH, static_cast<int>(a.n_vec - v0 < 64 ? a.n_vec - v0 : 64), lane);
+  }
+  for (; tile < n_tiles; tile += stride) {
+    const int64_t v0 = static_cast<int64_t>(tile) << 6;
     const int nv = static_cast<int>(a.n_vec - v0 < 64 ? a.n_vec - v0 : 64);
 
-    // 1. Coalesced load of the tile's 64 vectors (64*CH chunks), transposed through LDS.
-    //    Rows past the end of the input (last tile only) re-read row nv-1: every load is
-    //    in bounds and unconditional, and those lanes' results are never stored.
-    const uint4* src = reinterpret_cast<const uint4*>(a.x) + v0 * CH;
-    uint4 tmp[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int g = k * 64 + lane;
-      const int gc = (g / CH < nv) ? g : (nv - 1) * CH + g % CH;
-      tmp[k] = src[gc];
-    }
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int g = k * 64 + lane, row = g / CH, c = g % CH;
-      buf[row * CH + (c ^ swz<CH>(row))] = tmp[k];
-    }
-    wave_lds_fence();
-    uint32_t xh[D / 2];  // this lane's vector: fp16 pairs
+    // 1. The tile is in LDS once this wave's loads have landed; read this lane's row,
+    //    then start loading the next tile into the same buffer.
+    wait_vmem();
+    // `tile >> 31` is 0; it makes the lane's addresses loop-variant so they are recomputed
+    // (one instruction each) rather than held in 2*CH registers across the loop
+    const int rbase = rbase0 + (tile >> 31);
+    uint32_t xh[D / 2];  // this lane's vector: fp16 pairs, sign-flipped
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const uint4 q = buf[lane * CH + (c ^ swz<CH>(lane))];
-      xh[4 * c] = q.x; xh[4 * c + 1] = q.y; xh[4 * c + 2] = q.z; xh[4 * c + 3] = q.w;
+      const uint4 q = buf[rbase ^ c];
+      const uint4 m = smask[c + (tile >> 31)];  // same address in every lane: a broadcast
+      xh[4 * c] = q.x ^ m.x; xh[4 * c + 1] = q.y ^ m.y; xh[4 * c + 2] = q.z ^ m.z; xh[4 * c + 3] = q.w ^ m.w;
     }
-    wave_lds_fence();
+    wait_lds();
+    {
+      const int nt = tile + stride;
+      if (nt < n_tiles) {
+        const int64_t w0 = static_cast<int64_t>(nt) << 6;
+        dma_tile<CH>(buf, x16 + w0 * CH, static_cast<int>(a.n_vec - w0 < 64 ? a.n_vec - w0 : 64),
+                     lane + (tile >> 31));
+      }
+    }
 
     // 2. Norm: sum of squares of the fp16 inputs, four float32 accumulators.
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -191,72 +245,43 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
     }
     const float n = __builtin_sqrtf((acc[0] + acc[1]) + (acc[2] + acc[3]));
 
-    // 3. Sign-flipped Walsh-Hadamard transform, unnormalised, sign of coordinate 0 factored
-    //    out. Groups of G coordinates first run their in-group stages with the group's G-1
-    //    multipliers (one 16-dword scalar load, issued where the group starts so the
-    //    multipliers never all sit in SGPRs at once), then the cross-group stages run.
-    constexpr int G = D < 16 ? D : 16;
-    // `tile >> 62` is 0 for every real tile, but it makes the multiplier addresses depend
-    // on the loop, so the loads are issued per group inside the loop instead of being
-    // hoisted out of it with all d - 1 multipliers held in scalar registers at once.
-    const kargf_t tbase = karg_multipliers() + (tile >> 62);
+    // 3. Walsh-Hadamard transform of the sign-flipped vector, unnormalised: y' = H (s . x).
+    //    The first two butterfly stages of every 4 coordinates (fp16 pairs P0, P1) come
+    //    from v_dot2 with fp16 (+-1, +-1) weights and a float32 addend: s0 = P0.(1,1),
+    //    d0 = P0.(1,-1), then P1.(1,1) + s0, P1.(1,-1) + d0, P1.(-1,-1) + s0, P1.(-1,1) + d0:
+    //    6 instructions for 4 outputs, exact products. The remaining stages are float32
+    //    additions in registers.
     float y[D];
 #pragma unroll
-    for (int g = 0; g < D / G; ++g) {
-      const kargf_t tg = tbase + g * G;
-#pragma unroll
-      for (int m = 0; m < G / 2; ++m) {
-        const half2_t h = __builtin_bit_cast(half2_t, xh[g * G / 2 + m]);
-        const float lo = static_cast<float>(h.x), hi = static_cast<float>(h.y);
-        const float t = tg[m];
-        y[g * G + 2 * m] = __builtin_fmaf(hi, t, lo);
-        y[g * G + 2 * m + 1] = __builtin_fmaf(hi, -t, lo);
-      }
-      int off = G / 2;
-#pragma unroll
-      for (int h = 2; h < G; h <<= 1) {
-#pragma unroll
-        for (int p = 0; p < G / (2 * h); ++p) {
-          const float t = tg[off + p];
-#pragma unroll
-          for (int j = 0; j < h; ++j) {
-            float& u = y[g * G + p * 2 * h + j];
-            float& w = y[g * G + p * 2 * h + h + j];
-            const float uu = u;
-            u = __builtin_fmaf(w, t, uu);
-            w = __builtin_fmaf(w, -t, uu);
-          }
-        }
-        off += G / (2 * h);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < D / 4; ++q) {
+      const float s0 = dot2_f16(xh[2 * q], kPP, 0.0f, true);
+      const float d0 = dot2_f16(xh[2 * q], kPM, 0.0f, true);
+      y[4 * q] = dot2_f16(xh[2 * q + 1], kPP, s0, false);
+      y[4 * q + 1] = dot2_f16(xh[2 * q + 1], kPM, d0, false);
+      y[4 * q + 2] = dot2_f16(xh[2 * q + 1], kMM, s0, false);
+      y[4 * q + 3] = dot2_f16(xh[2 * q + 1], kMP, d0, false);
     }
-    if constexpr (D > G) {
-      const kargf_t tc = tbase + D;
-      int off = 0;
 #pragma unroll
-      for (int h = G; h < D; h <<= 1) {
+    for (int h = 4; h < D; h <<= 1) {
 #pragma unroll
-        for (int p = 0; p < D / (2 * h); ++p) {
-          const float t = tc[off + p];
+      for (int p = 0; p < D / (2 * h); ++p) {
 #pragma unroll
-          for (int j = 0; j < h; ++j) {
-            float& u = y[p * 2 * h + j];
-            float& w = y[p * 2 * h + h + j];
-            const float uu = u;
-            u = __builtin_fmaf(w, t, uu);
-            w = __builtin_fmaf(w, -t, uu);
-          }
+        for (int j = 0; j < h; ++j) {
+          const float u = y[p * 2 * h + j], w = y[p * 2 * h + h + j];
+          y[p * 2 * h + j] = u + w;
+          y[p * 2 * h + h + j] = u - w;
         }
-        off += D / (2 * h);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. Quantize both stages and pack. K maps the raw transform to the stage-1 unit with
     //    the sign flipped: NX = fma(y', -K, +0) = -(y_true * unit1). Adding +0 turns an exact
     //    zero into +0, so sign(NX) is exactly [y_true > 0] (the count semantics at the middle
-    //    boundary 0). A zero vector gets K = 0, so y_true = 0.
+    //    boundary 0). A zero vector gets K = 0, so y_true = 0. The stage-2 value
+    //    X2 = (|y_true| - cm) * unit2 is formed from y' directly (K2 = |K| * r12), one rounding.
     const float K = (n > 0.f) ? a.k_scale / n : 0.f;
+    const float K2 = __builtin_fabsf(K) * a.r12;
     uint32_t w1[NW], w2[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -271,14 +296,14 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
         if constexpr (BITS == 1) {
           // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
           u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
-          const float x2 = ax - a.cm2[0];
+          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -a.cm2[0]);
           u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
         } else if constexpr (BITS == 2) {
           // Unit 2/T1: bit 31 of NX is P = [y > 0], bit 30 is O = [|NX| >= 2] = [|y| >= T1].
           u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 30);
           const float cm = (ax >= 2.0f) ? a.cm2[1] : a.cm2[0];
           // residual magnitude |y| - cm in stage-2 units 2/T2: its sign bit is Q, bit 30 is [|r| >= T2]
-          const float x2 = __builtin_fmaf(ax, a.r12, -cm);
+          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -cm);
           u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 30);
         } else {
           // bucket tables: m = number of positive thresholds below |y|, in table units
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
           const bool gt = ax > e.x;
           u1 = (u1 << (BITS - 1)) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
           const float cm = gt ? e.w : e.z;
-          const float x2 = __builtin_fmaf(ax, a.r12, -cm);
+          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -cm);
           u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
           const float ax2 = __builtin_fabsf(x2);
           const int j2 = static_cast<int>(__builtin_fminf(ax2, static_cast<float>(a.j2max)));
@@ -321,7 +346,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
     // 5. Stores: each lane writes its own norm and 2 x NW words; lanes hold consecutive
     //    vectors, so a wave writes contiguous runs.
     if (lane < nv) {
-      const int64_t row = cache_row(a.map, v0, lane);
+      const int64_t row = cache_row<CONTIG>(a.map, v0, lane);
       a.norms[row] = n;
       store_words<NW>(a.p1 + row * NW, w1);
       store_words<NW>(a.p2 + row * NW, w2);
@@ -331,8 +356,8 @@ __global__ __launch_bounds__(kBlockThreads) void encode_l1(const EncodeArgs a) {
 
 // ------------------------------------------------------------------------------ decode
 
-template <int D, int BITS>
-__global__ __launch_bounds__(kBlockThreads) void decode_l1(const DecodeArgs a) {
+template <int D, int BITS, bool CONTIG>
+__global__ __launch_bounds__(kBlockThreads, 2) void decode_l1(const DecodeArgs a) {
   static_assert(D >= 8 && D <= 128 && (D & (D - 1)) == 0, "one vector per lane needs D <= 128");
   constexpr int CH = D / 8;
   constexpr int EPW = 32 / BITS;
@@ -341,8 +366,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_l1(const DecodeArgs a) {
   constexpr int NZ = 1 << (2 * BITS);
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
+  __shared__ uint4 smask[CH];  // per-pair fp16 sign masks, 8 pairs per 16 bytes
   __shared__ float zt[NZ];
   for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
+  for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -354,7 +381,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_l1(const DecodeArgs a) {
   for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wv; tile < n_tiles; tile += stride) {
     const int64_t v0 = tile << 6;
     const int nv = static_cast<int>(a.n_vec - v0 < 64 ? a.n_vec - v0 : 64);
-    const int64_t row = cache_row(a.map, v0, lane < nv ? lane : 0);
+    const int64_t row = cache_row<CONTIG>(a.map, v0, lane < nv ? lane : 0);
 
     uint32_t w1[NW], w2[NW];
     load_words<NW>(a.p1 + row * NW, w1);
@@ -387,13 +414,17 @@ __global__ __launch_bounds__(kBlockThreads) void decode_l1(const DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < D / 2; ++m) {
       const half2_t h = {static_cast<_Float16>(z[2 * m] * K), static_cast<_Float16>(z[2 * m + 1] * K)};
-      o[m] = __builtin_bit_cast(uint32_t, h) ^ a.xmask[m];
+      o[m] = __builtin_bit_cast(uint32_t, h);
     }
 
-    // transpose back through LDS and write the tile with coalesced 16-byte stores
+    // apply the final sign flip (exact XOR of fp16 sign bits; the mask reads are
+    // broadcasts), transpose back through LDS and write the tile with coalesced stores
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      buf[lane * CH + (c ^ swz<CH>(lane))] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    for (int c = 0; c < CH; ++c) {
+      const uint4 mk = smask[c + (tile >> 62)];
+      buf[lane * CH + (c ^ swz<CH>(lane))] =
+          make_uint4(o[4 * c] ^ mk.x, o[4 * c + 1] ^ mk.y, o[4 * c + 2] ^ mk.z, o[4 * c + 3] ^ mk.w);
+    }
     wave_lds_fence();
     uint4* dst = reinterpret_cast<uint4*>(a.x) + v0 * CH;
 #pragma unroll
@@ -411,15 +442,17 @@ __global__ __launch_bounds__(kBlockThreads) void decode_l1(const DecodeArgs a) {
 template <int D, int BITS>
 static hipError_t launch_encode_t(const EncodeArgs& a, int blocks, hipStream_t stream) {
   void* args[] = {const_cast<EncodeArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&encode_l1<D, BITS>), dim3(blocks), dim3(kBlockThreads),
-                         args, 0, stream);
+  const void* f = a.map.contiguous ? reinterpret_cast<const void*>(&encode_l1<D, BITS, true>)
+                                   : reinterpret_cast<const void*>(&encode_l1<D, BITS, false>);
+  return hipLaunchKernel(f, dim3(blocks), dim3(kBlockThreads), args, 0, stream);
 }
 
 template <int D, int BITS>
 static hipError_t launch_decode_t(const DecodeArgs& a, int blocks, hipStream_t stream) {
   void* args[] = {const_cast<DecodeArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_l1<D, BITS>), dim3(blocks), dim3(kBlockThreads),
-                         args, 0, stream);
+  const void* f = a.map.contiguous ? reinterpret_cast<const void*>(&decode_l1<D, BITS, true>)
+                                   : reinterpret_cast<const void*>(&decode_l1<D, BITS, false>);
+  return hipLaunchKernel(f, dim3(blocks), dim3(kBlockThreads), args, 0, stream);
 }
 
 #define KVQ_FOR_BITS(MACRO, D) \

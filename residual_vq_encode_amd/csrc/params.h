@@ -32,7 +32,7 @@ struct EncodeArgs {
   int64_t n_vec;
   RowMap map;
   // Per-vector scale: the quantizer works on X = y_true * unit, and the kernel forms
-  // -X = fma(y', -k_scale / n, +0) from the raw transform y' (see encode kernel).
+  // -X = fma(y', -k_scale / n, +0) from the raw transform y' = H diag(s) x.
   float k_scale;
   float r12;          // stage-2 units per stage-1 unit
   float cm2[2];       // bits <= 2: stage-1 centroid magnitudes in stage-2 units
@@ -41,14 +41,9 @@ struct EncodeArgs {
   // magnitude below/above the threshold in stage-2 units} and {threshold, count below}.
   float tab1[kTab1Max][4];
   float tab2[kTab2Max][2];
-  // One vector per lane: sign-carried butterfly multipliers. For each group of
-  // G = min(d, 16) coordinates, its G - 1 in-group multipliers (stage 1 first) padded to
-  // G; then the d/G - 1 cross-group multipliers, stage by stage. Several lanes per
-  // vector: per-pair XOR masks flipping fp16 sign bits.
-  union {
-    float t[144];
-    uint32_t xmask[512];
-  } sg;
+  // Per-pair XOR masks flipping fp16 sign bits: pair m covers coordinates 2m (bit 15)
+  // and 2m + 1 (bit 31).
+  uint32_t xmask[512];
 };
 
 struct DecodeArgs {

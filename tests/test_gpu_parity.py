@@ -156,7 +156,7 @@ def test_workload_decode_append():
         rows = steps[t].reshape(-1, D).cpu().numpy()
         rep, _ = gu.judge(rows, s, 2, gu.as_u32(p1[:, :, t]).reshape(-1, 8), gu.as_u32(p2[:, :, t]).reshape(-1, 8),
                           nrm[:, :, t].cpu().numpy().reshape(-1))
-        assert rep.ok(gu.MAX_FLIP_FRACTION, gu.NORM_REL_TOL), (t, rep.summary())
+        assert rep.ok(gu.flip_cap(rep.n_codes), gu.NORM_REL_TOL), (t, rep.summary())
     assert bool((p1[:, :, spec.S:] == -1).all()) and bool((p2[:, :, spec.S:] == -1).all())
     assert bool(torch.isnan(nrm[:, :, spec.S:]).all())
 
@@ -210,7 +210,7 @@ def test_cache_window(S, S_cap, s_offset):
     win = slice(s_offset, s_offset + S)
     rep, ref = gu.judge(x.cpu().numpy().reshape(-1, 128), s, 2, gu.as_u32(p1[:, :, win]).reshape(-1, 8),
                         gu.as_u32(p2[:, :, win]).reshape(-1, 8), nrm[:, :, win].cpu().numpy().reshape(-1))
-    assert rep.ok(gu.MAX_FLIP_FRACTION, gu.NORM_REL_TOL), rep.summary()
+    assert rep.ok(gu.flip_cap(rep.n_codes), gu.NORM_REL_TOL), rep.summary()
     outside = torch.ones(S_cap, dtype=torch.bool)
     outside[win] = False
     assert bool((p1[:, :, outside] == -1).all()) and bool((p2[:, :, outside] == -1).all())
