@@ -10,8 +10,8 @@
 #include "params.h"
 
 namespace kvq {
-hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int blocks, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int blocks, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs& a, int d, int bits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, int bits, hipStream_t stream);
 }  // namespace kvq
 
 namespace {
@@ -19,12 +19,6 @@ namespace {
 using kvq::DecodeArgs;
 using kvq::EncodeArgs;
 using kvq::RowMap;
-
-// Persistent grid: two 256-thread blocks per compute unit (the LDS tile buffers and the
-// register budget allow two resident blocks per CU; MI355X has 256 CUs), so every wave is
-// resident from the start and walks tiles of 64 vectors with a grid stride, loading its
-// next tile while it computes the current one.
-constexpr int kMaxBlocks = 2048;
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -70,12 +64,6 @@ RowMap row_map(int64_t S, int64_t S_cap, int64_t s_offset) {
   m.inv_S = 1.0f / static_cast<float>(m.S);
   m.contiguous = (S == S_cap && s_offset == 0) ? 1 : 0;
   return m;
-}
-
-int grid_blocks(int64_t n_vec) {
-  const int64_t tiles = (n_vec + 63) / 64;
-  const int64_t blocks = (tiles + kvq::kWavesPerBlock - 1) / kvq::kWavesPerBlock;
-  return static_cast<int>(blocks < kMaxBlocks ? blocks : kMaxBlocks);
 }
 
 // Bucket table for the positive thresholds of one stage (bits >= 3). The bucket width is
@@ -136,8 +124,7 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
     const double T1 = cb->b1[2], T2 = cb->b2[2];
     a->k_scale = static_cast<float>((2.0 / T1) * inv_sqrt_d);
     a->r12 = static_cast<float>(T1 / T2);
-    a->cm2[0] = static_cast<float>(cb->c1[2] * (2.0 / T2));
-    a->cm2[1] = static_cast<float>(cb->c1[3] * (2.0 / T2));
+    a->cm2[0] = static_cast<float>((static_cast<double>(cb->c1[3]) - cb->c1[2]) / T2);  // h in units 2/T2
   } else {
     Buckets b1, b2;
     if (!make_buckets(cb->b1, bits, &b1, kvq::kTab1Max) || !make_buckets(cb->b2, bits, &b2, kvq::kTab2Max))
@@ -188,7 +175,6 @@ extern "C" kvq_status kvq_rvq_encode_pack(const kvq_codebooks* cb, const uint16_
   if (n_vec == 0) return KVQ_OK;
   if (x == nullptr || packed1 == nullptr || packed2 == nullptr || norms == nullptr) return KVQ_ERR_ARG;
   if (!aligned(x, 16) || !aligned(packed1, 16) || !aligned(packed2, 16) || !aligned(norms, 4)) return KVQ_ERR_ALIGN;
-  if (cb->d > 128) return KVQ_ERR_SHAPE;
 
   EncodeArgs a;
   a.x = x;
@@ -199,7 +185,7 @@ extern "C" kvq_status kvq_rvq_encode_pack(const kvq_codebooks* cb, const uint16_
   a.map = row_map(S, S_cap, s_offset);
   st = fill_encode_args(cb, &a);
   if (st != KVQ_OK) return st;
-  const hipError_t e = kvq::launch_encode(a, cb->d, cb->bits, grid_blocks(n_vec), static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq::launch_encode(a, cb->d, cb->bits, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
@@ -216,7 +202,6 @@ extern "C" kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb, const uint3
   if (packed1 == nullptr || packed2 == nullptr || x_out == nullptr) return KVQ_ERR_ARG;
   if (!aligned(x_out, 16) || !aligned(packed1, 16) || !aligned(packed2, 16) || !aligned(norms, 4))
     return KVQ_ERR_ALIGN;
-  if (cb->d > 128) return KVQ_ERR_SHAPE;
 
   DecodeArgs a;
   a.p1 = packed1;
@@ -226,6 +211,6 @@ extern "C" kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb, const uint3
   a.n_vec = n_vec;
   a.map = row_map(S, S_cap, s_offset);
   fill_decode_args(cb, &a);
-  const hipError_t e = kvq::launch_decode(a, cb->d, cb->bits, grid_blocks(n_vec), static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq::launch_decode(a, cb->d, cb->bits, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }

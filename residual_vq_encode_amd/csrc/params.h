@@ -35,7 +35,9 @@ struct EncodeArgs {
   // -X = fma(y', -k_scale / n, +0) from the raw transform y' = H diag(s) x.
   float k_scale;
   float r12;          // stage-2 units per stage-1 unit
-  float cm2[2];       // bits <= 2: stage-1 centroid magnitudes in stage-2 units
+  float cm2[2];       // bits = 1: cm2[0] = stage-1 centroid magnitude in stage-2 units;
+                      // bits = 2: cm2[0] = half the gap between the two centroid magnitudes,
+                      // in stage-2 units
   int32_t j1max, j2max;  // bits >= 3: last bucket index of each table
   // bits >= 3 bucket tables: {threshold, count below the bucket (int bits), centroid
   // magnitude below/above the threshold in stage-2 units} and {threshold, count below}.

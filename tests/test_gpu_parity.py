@@ -21,7 +21,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-D_ONE_LANE = [8, 16, 32, 64, 128]
+D_ALL = [8, 16, 32, 64, 128, 256, 512, 1024]
 
 
 def _say(msg):
@@ -47,7 +47,7 @@ def test_worked_examples_on_gpu():
 
 # ------------------------------------------------------------------------- pages' grid
 
-@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("d", D_ALL)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("n", [1, 5, 33])
 def test_parity_grid(d, bits, n):
@@ -57,7 +57,7 @@ def test_parity_grid(d, bits, n):
     gu.check_encode(x, _signs(1000 + d, d), bits)
 
 
-@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("d", D_ALL)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_decode_grid(d, bits):
     _say(f"decode d={d} bits={bits}")
@@ -71,11 +71,22 @@ def test_decode_grid(d, bits):
 # ------------------------------------------------------------------------- tiles and tails
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("n", [63, 64, 65, 127, 129, 1000, 4097, 70001])
+@pytest.mark.parametrize("n", [15, 16, 17, 63, 64, 65, 127, 129, 1000, 4097, 70001])
 def test_ragged_tiles(bits, n):
-    _say(f"ragged bits={bits} n={n}")
+    _say(f"ragged d=128 bits={bits} n={n}")
     spec = synth.TensorSpec(1, 1, n, 128, "gauss_outliers", 31 + n)
     gu.check_encode(synth.tensor(spec, device=DEV), _signs(5, 128), bits)
+
+
+@pytest.mark.parametrize("d,n", [(8, 600001), (16, 300007), (32, 200003), (64, 150001), (256, 33333),
+                                 (512, 9999), (1024, 4999)])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_many_tiles_per_wave(d, n, bits):
+    """More tiles than the resident grid holds waves, so waves loop (and prefetch), with a
+    ragged last tile."""
+    _say(f"many tiles d={d} bits={bits} n={n}")
+    spec = synth.TensorSpec(1, 1, n, d, "gauss", 900 + d + bits)
+    gu.check_encode(synth.tensor(spec, device=DEV), _signs(6 + d, d), bits)
 
 
 # ------------------------------------------------------------------------- workloads
@@ -183,7 +194,7 @@ def _degenerate_rows(d):
     return np.stack(rows).astype(np.float16)
 
 
-@pytest.mark.parametrize("d", D_ONE_LANE)
+@pytest.mark.parametrize("d", D_ALL)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("sign_kind", ["plus", "random"])
 def test_degenerate_inputs(d, bits, sign_kind):
