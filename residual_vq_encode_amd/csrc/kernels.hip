@@ -89,20 +89,34 @@ constexpr int kNonTemporal = 2;
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// fp16x2 dot product with a float32 addend, the non-accumulating (VOP3P) form: the
+// fp16x2 dot products with a float32 addend, the non-accumulating (VOP3P) form: the
 // compiler otherwise picks the accumulating v_dot2c and spends a move zeroing each
-// destination. `w` holds two fp16 weights (low half weighs the pair's first element).
-constexpr uint32_t kPP = 0x3C003C00u;  // (+1, +1)
-constexpr uint32_t kPM = 0xBC003C00u;  // (+1, -1)
-constexpr uint32_t kMM = 0xBC00BC00u;  // (-1, -1)
-constexpr uint32_t kMP = 0x3C00BC00u;  // (-1, +1)
-__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w, float addend, bool zero_addend) {
+// destination. `w` holds two fp16 weights (low half weighs the pair's first element);
+// NEG selects the VOP3P source modifiers applied to it: 0 = (w0, w1), 1 = (w0, -w1),
+// 2 = (-w0, -w1), 3 = (-w0, w1). With w = (s_a, s_b), the rotation's signs for the pair,
+// this multiplies the pair by (+-s_a, +-s_b) exactly: the sign flip costs nothing.
+constexpr uint32_t kPP = 0x3C003C00u;  // fp16 (+1, +1)
+
+template <int NEG>
+__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w) {
   float r;
-  if (zero_addend) {
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(pair), "s"(w));
-  } else {
-    asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "s"(w), "v"(addend));
-  }
+  if constexpr (NEG == 0) asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(pair), "v"(w));
+  if constexpr (NEG == 1) asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
+  if constexpr (NEG == 2)
+    asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_lo:[0,1,0] neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
+  if constexpr (NEG == 3) asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_lo:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
+  return r;
+}
+template <int NEG>
+__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w, float addend) {
+  float r;
+  if constexpr (NEG == 0) asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
+  if constexpr (NEG == 1)
+    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
+  if constexpr (NEG == 2)
+    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_lo:[0,1,0] neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
+  if constexpr (NEG == 3)
+    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_lo:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
   return r;
 }
 
@@ -221,12 +235,21 @@ __device__ __forceinline__ void lane_stages(float (&y)[C]) {
 template <int CH>
 __device__ __forceinline__ void dma_tile(uint4* buf, const uint4* src, int nrows, int lane) {
   const char* base = reinterpret_cast<const char*>(src);  // wave-uniform
+  if (nrows == 64) {
 #pragma unroll
-  for (int k = 0; k < CH; ++k) {
-    const int slot = k * 64 + lane, r = slot / CH, c = (slot % CH) ^ swz<CH>(r);
-    const int rr = r < nrows ? r : nrows - 1;
-    const uint32_t off = static_cast<uint32_t>(rr * CH + c) * 16u;
-    __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, kNonTemporal);
+    for (int k = 0; k < CH; ++k) {
+      const int slot = k * 64 + lane, r = slot / CH, c = (slot % CH) ^ swz<CH>(r);
+      const uint32_t off = static_cast<uint32_t>(r * CH + c) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, kNonTemporal);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int slot = k * 64 + lane, r = slot / CH, c = (slot % CH) ^ swz<CH>(r);
+      const int rr = r < nrows ? r : nrows - 1;
+      const uint32_t off = static_cast<uint32_t>(rr * CH + c) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, kNonTemporal);
+    }
   }
 }
 
@@ -353,11 +376,9 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   constexpr int CSTREAM = 64 * C / 4 + 4;            // STAGED: dwords per code stream (+ read pad)
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
-  __shared__ uint4 smask[D / 8];  // per-pair fp16 sign masks, 8 coordinates per 16 bytes
   __shared__ float4 t1s[BITS >= 3 ? kTab1Max : 1];
   __shared__ float2 t2s[BITS >= 3 ? kTab2Max : 1];
   __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? 2 * CSTREAM : 1];
-  for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   if constexpr (BITS >= 3) {
     for (int i = threadIdx.x; i < kTab1Max; i += kBlockThreads)
       t1s[i] = make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3]);
@@ -379,6 +400,10 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   const int rbase = lane * CH + swz<CH>(lane);
   // the transform of lane q comes out multiplied by (-1)^popcount(q) (see cross_stage)
   const bool negated = (__builtin_popcount(q) & 1) != 0;
+  // fp16 weights (s_2p, s_2p+1) of this lane's C/2 coordinate pairs: the rotation's signs
+  uint32_t wt[C / 2];
+#pragma unroll
+  for (int p = 0; p < C / 2; ++p) wt[p] = kPP ^ a.xmask[q * (C / 2) + p];
 
   int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
   if (tile < n_tiles) {
@@ -401,18 +426,17 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
     //    coordinates chunk by chunk; each chunk (8 coordinates) goes straight into the
     //    squared norm and into the first two butterfly stages.
     //    Walsh-Hadamard transform of the sign-flipped vector, unnormalised: y' = H (s . x).
-    //    Stages 1-2 of every 4 coordinates (fp16 pairs P0, P1) come from v_dot2 with fp16
-    //    (+-1, +-1) weights and a float32 addend: s0 = P0.(1,1), d0 = P0.(1,-1), then
-    //    P1.(1,1) + s0, P1.(1,-1) + d0, P1.(-1,-1) + s0, P1.(-1,1) + d0: 6 instructions for
-    //    4 outputs, exact products.
+    //    Stages 1-2 of every 4 coordinates (fp16 pairs P0, P1 with sign weights W0, W1)
+    //    come from v_dot2 with a float32 addend: s0 = P0.W0, d0 = P0.(W0 with the second
+    //    weight negated), then P1.W1 + s0, P1.(w, -w) + d0, P1.(-w, -w) + s0,
+    //    P1.(-w, w) + d0: 6 instructions for 4 outputs, exact products.
     wait_vmem();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float y[C];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const uint4 v = buf[rbase ^ c];
-      const uint4 m = smask[q * CH + c];  // the same address for every lane of a vector slot
-      const uint32_t xh[4] = {v.x ^ m.x, v.y ^ m.y, v.z ^ m.z, v.w ^ m.w};
+      const uint32_t xh[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const half2_t h = __builtin_bit_cast(half2_t, xh[i]);
@@ -420,13 +444,14 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const float s0 = dot2_f16(xh[2 * g], kPP, 0.0f, true);
-        const float d0 = dot2_f16(xh[2 * g], kPM, 0.0f, true);
+        const uint32_t w0 = wt[4 * c + 2 * g], w1 = wt[4 * c + 2 * g + 1];
+        const float s0 = dot2_f16<0>(xh[2 * g], w0);
+        const float d0 = dot2_f16<1>(xh[2 * g], w0);
         float* o = y + 8 * c + 4 * g;
-        o[0] = dot2_f16(xh[2 * g + 1], kPP, s0, false);
-        o[1] = dot2_f16(xh[2 * g + 1], kPM, d0, false);
-        o[2] = dot2_f16(xh[2 * g + 1], kMM, s0, false);
-        o[3] = dot2_f16(xh[2 * g + 1], kMP, d0, false);
+        o[0] = dot2_f16<0>(xh[2 * g + 1], w1, s0);
+        o[1] = dot2_f16<1>(xh[2 * g + 1], w1, d0);
+        o[2] = dot2_f16<2>(xh[2 * g + 1], w1, s0);
+        o[3] = dot2_f16<3>(xh[2 * g + 1], w1, d0);
       }
     }
     wait_lds();
