@@ -430,6 +430,10 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
     //    come from v_dot2 with a float32 addend: s0 = P0.W0, d0 = P0.(W0 with the second
     //    weight negated), then P1.W1 + s0, P1.(w, -w) + d0, P1.(-w, -w) + s0,
     //    P1.(-w, w) + d0: 6 instructions for 4 outputs, exact products.
+    // The wave raises its issue priority while it drains LDS and issues the next tile's
+    // loads and the previous tile's stores, so those requests leave early, and drops it
+    // again for the arithmetic.
+    __builtin_amdgcn_s_setprio(2);
     wait_vmem();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float y[C];
@@ -483,6 +487,8 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
         dma_tile<CH>(buf, x16 + static_cast<int64_t>(nt) * 64 * CH, nvn * L, lane);
       }
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // 3. Remaining butterfly stages: in registers, then across the vector's lanes.
     lane_stages<C, 4>(y);
@@ -662,18 +668,55 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   const int stride = static_cast<int>(gridDim.x) * kWavesPerBlock;
   const bool negated = (__builtin_popcount(q) & 1) != 0;
 
-  for (int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv; tile < n_tiles; tile += stride) {
+  // Software pipeline: the packed words and norm of the next tile are loaded into
+  // registers while the current tile is computed, and the current tile's output is stored
+  // at the start of the next iteration, after those loads have been issued.
+  uint32_t nw1[NWL], nw2[NWL];  // next tile's words (STAGED: words q, q + L, ... of the vector)
+  float nnrm = 1.0f;
+  auto fetch = [&](int t) {
+    const int64_t t0 = static_cast<int64_t>(t) * VW;
+    const int tnv = static_cast<int>(a.n_vec - t0 < VW ? a.n_vec - t0 : VW);
+    // lanes past the last vector read vector t0 (valid) and store nothing
+    const int64_t row = cache_row<CONTIG>(a.map, t0, vl < tnv ? vl : 0);
+    if constexpr (STAGED) {
+#pragma unroll
+      for (int k = 0; k < NWL; ++k) {
+        const int w = q + L * k < NW ? q + L * k : NW - 1;
+        nw1[k] = a.p1[row * NW + w];
+        nw2[k] = a.p2[row * NW + w];
+      }
+    } else {
+      load_words<NWL>(a.p1 + row * NW + q * NWL, nw1);
+      load_words<NWL>(a.p2 + row * NW + q * NWL, nw2);
+    }
+    nnrm = a.norms ? a.norms[row] : 1.0f;
+  };
+  u32x4_t out[CH];          // previous tile's output chunks (chunk 64k + lane of that tile)
+  int out_tile = -1, out_rows = 0;
+  auto flush = [&]() {
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x) + static_cast<int64_t>(out_tile) * 64 * CH;
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+      if ((k * 64 + lane) / CH < out_rows) __builtin_nontemporal_store(out[k], dst + k * 64 + lane);
+  };
+
+  int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
+  if (tile < n_tiles) fetch(tile);
+  for (; tile < n_tiles; tile += stride) {
     const int64_t v0 = static_cast<int64_t>(tile) * VW;
     const int nv = static_cast<int>(a.n_vec - v0 < VW ? a.n_vec - v0 : VW);
-    // lanes past the last vector decode vector v0 (valid) and store nothing
-    const int64_t row = cache_row<CONTIG>(a.map, v0, vl < nv ? vl : 0);
+    __builtin_amdgcn_s_setprio(2);
+    uint32_t w1[NWL], w2[NWL];
+#pragma unroll
+    for (int k = 0; k < NWL; ++k) { w1[k] = nw1[k]; w2[k] = nw2[k]; }
+    const float nrm = nnrm;
+    if (out_tile >= 0) flush();
+    if (tile + stride < n_tiles) fetch(tile + stride);
+    __builtin_amdgcn_s_setprio(0);
 
     // 1. Codes of this lane's C coordinates, as (i1, i2) pairs -> z = c1[i1] + c2[i2].
     float z[C];
     if constexpr (!STAGED) {
-      uint32_t w1[NWL], w2[NWL];
-      load_words<NWL>(a.p1 + row * NW + q * NWL, w1);
-      load_words<NWL>(a.p2 + row * NW + q * NWL, w2);
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         const uint32_t i1 = (w1[j / EPW] >> (BITS * (j % EPW))) & MASK;
@@ -681,7 +724,7 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
         z[j] = zt[(i1 << BITS) | i2];
       }
     } else {
-      // lane q of a vector unpacks words q, q + L, ... into one byte per code in LDS
+      // lane q of a vector unpacks its words q, q + L, ... into one byte per code in LDS
       uint32_t* cs = cstage[wv];
 #pragma unroll
       for (int k = 0; k < NWL; ++k) {
@@ -691,7 +734,7 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
           const int cnt = D - 10 * w < 10 ? D - 10 * w : 10;  // even
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const uint32_t wd = (st == 0 ? a.p1 : a.p2)[row * NW + w];
+            const uint32_t wd = st == 0 ? w1[k] : w2[k];
             const uint32_t e0 = unpack4x3(wd), e1 = unpack4x3(wd >> 12), e2 = unpack4x3(wd >> 24);
             uint16_t* h = reinterpret_cast<uint16_t*>(cs + st * CSTREAM) + (base >> 1);
             const uint16_t hv[5] = {static_cast<uint16_t>(e0), static_cast<uint16_t>(e0 >> 16),
@@ -715,7 +758,6 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
       }
       wave_lds_fence();
     }
-    const float nrm = a.norms ? a.norms[row] : 1.0f;
 
     // 2. Inverse rotation: H z (H symmetric), in registers then across lanes; then the
     //    scale n / sqrt(D) (carrying the lane's sign) and the final sign flip.
@@ -730,8 +772,8 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
       o[m] = __builtin_bit_cast(uint32_t, h);
     }
 
-    // 3. Exact sign flip (XOR of fp16 sign bits), transpose through LDS, and write the tile
-    //    with coalesced 16-byte stores (it is contiguous in the output).
+    // 3. Exact sign flip (XOR of fp16 sign bits) and transpose through LDS into the chunk
+    //    order of the (contiguous) output tile, for coalesced 16-byte stores.
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const uint4 mk = smask[q * CH + c];
@@ -739,16 +781,17 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
           make_uint4(o[4 * c] ^ mk.x, o[4 * c + 1] ^ mk.y, o[4 * c + 2] ^ mk.z, o[4 * c + 3] ^ mk.w);
     }
     wave_lds_fence();
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x) + static_cast<int64_t>(tile) * 64 * CH;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int g = k * 64 + lane, r = g / CH, c = g % CH;
       const uint4 v = buf[r * CH + (c ^ swz<CH>(r))];
-      const u32x4_t vv = {v.x, v.y, v.z, v.w};
-      if (r < nv * L) __builtin_nontemporal_store(vv, dst + g);
+      out[k] = u32x4_t{v.x, v.y, v.z, v.w};
     }
     wave_lds_fence();
+    out_tile = tile;
+    out_rows = nv * L;
   }
+  if (out_tile >= 0) flush();
 }
 
 // ------------------------------------------------------------------------------ dispatch
