@@ -39,10 +39,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30  # --copy-calibration: one plain device copy reads and writes this many bytes
 WORKLOADS = {
-    # name: (tensor preset in synth.WORKLOADS, bits, pool size)
-    "llama_layer": ("llama_layer", 2, 8),
-    "gqa_long_b1": ("gqa_long", 1, 8),
-    "gqa_long_b4": ("gqa_long", 4, 8),
+    # name: (tensor preset in synth.WORKLOADS, bits, pool size, stages)
+    "llama_layer": ("llama_layer", 2, 8, 2),
+    "gqa_long_b1": ("gqa_long", 1, 8, 2),
+    "gqa_long_b4": ("gqa_long", 4, 8, 2),
+    "prefill_kv_b4": ("prefill_kv", 4, 2, 2),
+    # the single-stage codec (stage 1 only, one code stream) on the Llama layer
+    "llama_layer_mse": ("llama_layer", 2, 8, 1),
 }
 
 
@@ -53,7 +56,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(spec, signs, bits, target_s: float = 15.0) -> dict:
+def cpu_baseline(spec, signs, bits, stages: int = 2, target_s: float = 15.0) -> dict:
     """The oracle, as it stands, on a contiguous sample of the workload's first tensor."""
     import numpy as np
     import synth
@@ -61,18 +64,19 @@ def cpu_baseline(spec, signs, bits, target_s: float = 15.0) -> dict:
     from oracle import rvq
     t = ocb.build_tables(spec.D, bits)
     s = np.asarray(signs, np.int8)
+    run = rvq.encode if stages == 2 else rvq.encode_mse
     probe = synth.rows(spec, 0, 8192).numpy()
     t0 = time.perf_counter()
-    rvq.encode(probe, s, t)
+    run(probe, s, t)
     dt_probe = time.perf_counter() - t0
     n = int(min(spec.rows, max(8192, 8192 * target_s / max(dt_probe, 1e-3))))
     n = (n // 8192) * 8192
     x = synth.rows(spec, 0, n).numpy()
     t0 = time.perf_counter()
-    rvq.encode(x, s, t)
+    run(x, s, t)
     dt = time.perf_counter() - t0
     nw = -(-spec.D // (32 // bits))
-    nbytes = n * (spec.D * 2 + 2 * nw * 4)
+    nbytes = n * (spec.D * 2 + stages * nw * 4)
     try:
         import threadpoolctl
         cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
@@ -159,7 +163,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
-    wname, bits, pool_default = WORKLOADS[args.workload]
+    wname, bits, pool_default, stages = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wname]
     spec = w.tensors[0]
     P = args.pool or pool_default
@@ -187,10 +191,22 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
+    if stages == 2:
+        def enc(j):
+            kvq.kvq_rvq_encode_pack(cb, xs[j], p1s[j], p2s[j], ns[j], 0, stream)
+
+        def dec(j):
+            kvq.kvq_rvq_unpack_decode(cb, p1s[j], p2s[j], ns[j], outs[j], 0, stream)
+    else:
+        def enc(j):
+            kvq.kvq_mse_encode_pack(cb, xs[j], p1s[j], ns[j], 0, stream)
+
+        def dec(j):
+            kvq.kvq_mse_unpack_decode(cb, p1s[j], ns[j], outs[j], 0, stream)
+
     for i in range(args.warmup):
-        j = i % P
-        kvq.kvq_rvq_encode_pack(cb, xs[j], p1s[j], p2s[j], ns[j], 0, stream)
-        kvq.kvq_rvq_unpack_decode(cb, p1s[j], p2s[j], ns[j], outs[j], 0, stream)
+        enc(i % P)
+        dec(i % P)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -199,12 +215,10 @@ def main() -> int:
     wall0 = time.perf_counter()
     e0.record(stream)
     for i in range(K):
-        j = (args.warmup + i) % P
-        kvq.kvq_rvq_encode_pack(cb, xs[j], p1s[j], p2s[j], ns[j], 0, stream)
+        enc((args.warmup + i) % P)
     e1.record(stream)
     for i in range(K):
-        j = (args.warmup + i) % P
-        kvq.kvq_rvq_unpack_decode(cb, p1s[j], p2s[j], ns[j], outs[j], 0, stream)
+        dec((args.warmup + i) % P)
     e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -213,8 +227,8 @@ def main() -> int:
     dec_us = e1.elapsed_time(e2) * 1e3 / K
     total_ms = e0.elapsed_time(e2)
     n_vec = B * H * S
-    enc_bytes = n_vec * (D * 2 + 2 * nw * 4)
-    dec_bytes = n_vec * (2 * nw * 4 + 4 + D * 2)
+    enc_bytes = n_vec * (D * 2 + stages * nw * 4)
+    dec_bytes = n_vec * (stages * nw * 4 + 4 + D * 2)
     enc_gbps = enc_bytes / (enc_us * 1e-6) / 1e9
     dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
 
@@ -222,13 +236,19 @@ def main() -> int:
     from oracle import codebooks as ocb
     from oracle import flips, rvq
     j = (args.warmup + K - 1) % P
-    idx = torch.arange(0, n_vec, max(1, n_vec // 4096))
+    # a strided sample of 65536 vectors (the whole tensor when smaller): the flip cap is a
+    # rate, and a sample of ~10^7 codes estimates it without small-sample noise
+    idx = torch.arange(0, n_vec, max(1, n_vec // 65536))
     rows = xs[j].reshape(-1, D)[idx.to(dev)].cpu().numpy()
     t = ocb.build_tables(D, bits)
-    ref = rvq.encode(rows, signs, t)
-    rep = flips.compare_encode(p1s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32),
-                               p2s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32),
-                               ns[j].reshape(-1)[idx.to(dev)].cpu().numpy(), ref, t, 1e-5)
+    dev_p1 = p1s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
+    dev_n = ns[j].reshape(-1)[idx.to(dev)].cpu().numpy()
+    if stages == 2:
+        ref = rvq.encode(rows, signs, t)
+        rep = flips.compare_encode(dev_p1, p2s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32),
+                                   dev_n, ref, t, 1e-5)
+    else:
+        rep = flips.compare_encode_single(dev_p1, dev_n, rvq.encode_mse(rows, signs, t), t, 1e-5)
     parity_ok = rep.ok(max(1e-6, 1.0 / max(1, rep.n_codes)), 1e-6)
 
     traffic, _ = traffic_for(args.workload)
@@ -245,7 +265,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator; no dataset)",
-        "config": {"workload": f"{wname}: {w.note}", "shape": [B, H, S, D], "bits": bits,
+        "config": {"workload": f"{args.workload}: {w.note}" + ("" if stages == 2 else "; single-stage codec"),
+                   "shape": [B, H, S, D], "bits": bits, "stages": stages,
                    "pool_tensors": P, "step": "encode+pack then unpack+decode of one tensor"},
         "pct_of_hbm_peak": round(100.0 * enc_gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(B * S / (enc_us * 1e-6), 1),
@@ -258,10 +279,10 @@ def main() -> int:
         "parity_recheck": {"vectors": int(len(idx)), "flip_fraction": rep.flip_fraction, "ok": bool(parity_ok)},
         "roofline": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": enc_bytes, "kernel": f"kvq::encode_kernel<{D}, {bits}, true>"},
+                     "algorithmic_bytes_per_launch": enc_bytes, "kernel": f"kvq::encode_kernel<{D}, {bits}, true, {stages}>"},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, signs, bits)
+        result["cpu_baseline"] = cpu_baseline(spec, signs, bits, stages)
     print(json.dumps(result), flush=True)
     return 0 if parity_ok else 1
 

@@ -130,6 +130,33 @@ kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb,
                                  int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
                                  uint16_t* x_out, void* stream);
 
+/*
+ * kvq_mse_encode_pack - device. The single-stage codec: the same normalisation, rotation
+ * and stage-1 Gaussian Lloyd-Max quantization as kvq_rvq_encode_pack, without the residual
+ * stage (blog, "turboquant" tag page, "Kernel 3": randomized Hadamard rotation followed by
+ * the nearest-centroid quantize; counting boundary crossings gives the same index, "rvq"
+ * tag page, "What 'quantize' means here, precisely"). Only cb's c1/b1 tables and signs
+ * are used.
+ *   packed    device uint32 [B, H, S_cap, n_words], 16-byte aligned: the codes, with the
+ *             word layout of kvq_rvq_encode_pack's packed1 (and the same values)
+ *   other arguments and errors as for kvq_rvq_encode_pack
+ */
+kvq_status kvq_mse_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
+                               int64_t B, int64_t H, int64_t S,
+                               uint32_t* packed, float* norms,
+                               int64_t S_cap, int64_t s_offset, void* stream);
+
+/*
+ * kvq_mse_unpack_decode - device. Inverse of kvq_mse_encode_pack: each coordinate is
+ * dequantized as c1[i] (blog, "turboquant" tag page, "Kernel 2", dequantize: a gather of
+ * the centroid), rotated back by diag(s) H / sqrt(d), scaled by the norm (or not, for
+ * norms = NULL) and rounded to fp16 (nearest-even). Arguments and errors as for
+ * kvq_rvq_unpack_decode with the single code stream `packed`.
+ */
+kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed, const float* norms,
+                                 int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
+                                 uint16_t* x_out, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* kvq_status_str(kvq_status status);
 

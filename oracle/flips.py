@@ -103,3 +103,21 @@ def compare_encode(dev_p1: np.ndarray, dev_p2: np.ndarray, dev_norms: np.ndarray
     rel_err = np.where(nr > 0, dn / np.where(nr > 0, nr, 1.0), dn)
     rep.norm_max_rel = float(rel_err.max()) if rel_err.size else 0.0
     return rep
+
+
+def compare_encode_single(dev_p: np.ndarray, dev_norms: np.ndarray, ref: dict, t: Tables,
+                          rel: float = 1e-5) -> Report:
+    """The same rule for the single-stage codec: one stream, stage-1 codes only."""
+    n, d = ref["y"].shape
+    rep = Report(n_vectors=n, n_codes=n * d)
+    rep.padding_bad = int(np.count_nonzero(dev_p & packing.padding_mask(d, t.bits)))
+    i1d = packing.unpack(dev_p, t.bits, d)
+    y = ref["y"]
+    rep.stage1_diff, rep.bad_stage1, _, bad1 = _judge(y, i1d, ref["i1"], t.b1, t.sigma1, rel)
+    for (vi, ci) in np.argwhere(bad1)[:5]:
+        rep.examples.append(("stage1", int(vi), int(ci), float(y[vi, ci]), int(i1d[vi, ci]), int(ref["i1"][vi, ci])))
+    nr = ref["norm64"]
+    dn = np.abs(np.asarray(dev_norms, dtype=np.float64) - nr)
+    rel_err = np.where(nr > 0, dn / np.where(nr > 0, nr, 1.0), dn)
+    rep.norm_max_rel = float(rel_err.max()) if rel_err.size else 0.0
+    return rep

@@ -18,6 +18,8 @@ Per head vector x (fp16, length D), following the VeloxQuant-MLX blog:
   4. r = y - c1[i1], one float32 subtraction.  ["rvq" tag page, "The kernel".]
   5. i2 = index of the nearest stage-2 centroid to r.
   6. each code stream packed LSB-first into uint32 words (packing.py).
+Single-stage variant (encode_mse / decode_mse): steps 1-3 and 6 for one stream; decode
+z = c1[i1].
 Decode ("turboquant" tag page, "Kernel 5": the dequantized coordinate is
 c1[i1] + c2[i2], in the rotated domain):
   z = c1[i1] + c2[i2] (float32 add);  u_hat = diag(s) H z / sqrt(D)  (the inverse of step 2,
@@ -132,12 +134,9 @@ def encode(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
     }
 
 
-def decode(packed1: np.ndarray, packed2: np.ndarray, norms, signs: np.ndarray, t: Tables) -> np.ndarray:
-    """Decode [N, n_words] streams to float16 [N, D]; norms=None gives unit reconstructions."""
-    d = t.d
-    i1 = packing.unpack(packed1, t.bits, d)
-    i2 = packing.unpack(packed2, t.bits, d)
-    z = (t.c1[i1] + t.c2[i2]).astype(np.float32)
+def _unrotate(z: np.ndarray, norms, signs: np.ndarray, d: int) -> np.ndarray:
+    """x_hat = RN16(n * diag(s) H z / sqrt(D)) (RN16(diag(s) H z / sqrt(D)) for norms=None),
+    products and sums in float64, rounded once."""
     H = _H(d)
     s = np.asarray(signs, dtype=np.float64)
     w = (z.astype(np.float64) @ H.T) / math.sqrt(d)
@@ -145,3 +144,34 @@ def decode(packed1: np.ndarray, packed2: np.ndarray, norms, signs: np.ndarray, t
     if norms is not None:
         u_hat = u_hat * np.asarray(norms, dtype=np.float32).astype(np.float64)[:, None]
     return u_hat.astype(np.float16)
+
+
+def decode(packed1: np.ndarray, packed2: np.ndarray, norms, signs: np.ndarray, t: Tables) -> np.ndarray:
+    """Decode [N, n_words] streams to float16 [N, D]; norms=None gives unit reconstructions."""
+    d = t.d
+    i1 = packing.unpack(packed1, t.bits, d)
+    i2 = packing.unpack(packed2, t.bits, d)
+    z = (t.c1[i1] + t.c2[i2]).astype(np.float32)
+    return _unrotate(z, norms, signs, d)
+
+
+def encode_mse(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
+    """Single-stage encode: normalize, rotate, nearest stage-1 (Gaussian Lloyd-Max)
+    centroid, pack one stream.  ["turboquant" tag page, "Kernel 3": the rotation followed
+    by the nearest-centroid quantize; the cache keeps the unit vector's codes and its norm
+    as in the two-stage codec.]  Returns the packed stream, norms and intermediates."""
+    x16 = np.asarray(x16, dtype=np.float16)
+    if x16.ndim != 2 or x16.shape[1] != t.d:
+        raise ValueError("x16 must be [N, D] with D matching the tables")
+    norm, y = norms_and_rotation(x16, signs)
+    i1 = np.empty(y.shape, dtype=np.uint8)
+    for a in range(0, y.shape[0], CHUNK):
+        i1[a:a + CHUNK] = nearest(y[a:a + CHUNK], t.c1)
+    return {"packed": packing.pack(i1, t.bits), "norms": norm.astype(np.float32), "norm64": norm, "y": y, "i1": i1}
+
+
+def decode_mse(packed: np.ndarray, norms, signs: np.ndarray, t: Tables) -> np.ndarray:
+    """Single-stage decode: z = c1[i] ("turboquant" tag page, "Kernel 2": dequantize is a
+    gather of the centroid), then the inverse rotation and the norm."""
+    i1 = packing.unpack(packed, t.bits, t.d)
+    return _unrotate(t.c1[i1].astype(np.float32), norms, signs, t.d)

@@ -11,7 +11,9 @@ tensors are not on a GPU, the calls raise.
     x_hat = decode(p1, p2, norms, cb)                      # fp16 [B, H, S, D]
 
 The lower-level calls kvq_rvq_encode_pack / kvq_rvq_unpack_decode mirror the C ABI
-(including S_cap / s_offset for writing into and reading from a preallocated cache).
+(including S_cap / s_offset for writing into and reading from a preallocated cache);
+kvq_mse_encode_pack / kvq_mse_unpack_decode (and encode_mse / decode_mse) are the
+single-stage codec: stage 1 only, one code stream.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ from typing import Optional
 
 __all__ = [
     "KvqError", "Codebooks", "load", "library_path", "build_codebooks", "kvq_build_codebooks",
-    "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str", "encode", "decode", "n_words",
+    "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_mse_encode_pack", "kvq_mse_unpack_decode",
+    "kvq_status_str", "encode", "decode", "encode_mse", "decode_mse", "n_words",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.kvq_rvq_encode_pack.restype = ctypes.c_int
     lib.kvq_rvq_unpack_decode.argtypes = [ctypes.POINTER(Codebooks), ptr, ptr, ptr, i64, i64, i64, i64, i64, ptr, ptr]
     lib.kvq_rvq_unpack_decode.restype = ctypes.c_int
+    lib.kvq_mse_encode_pack.argtypes = [ctypes.POINTER(Codebooks), ptr, i64, i64, i64, ptr, ptr, i64, i64, ptr]
+    lib.kvq_mse_encode_pack.restype = ctypes.c_int
+    lib.kvq_mse_unpack_decode.argtypes = [ctypes.POINTER(Codebooks), ptr, ptr, i64, i64, i64, i64, i64, ptr, ptr]
+    lib.kvq_mse_unpack_decode.restype = ctypes.c_int
     lib.kvq_status_str.argtypes = [ctypes.c_int]
     lib.kvq_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -200,4 +207,64 @@ def decode(packed1, packed2, norms, cb: Codebooks, stream=None):
     B, H, S, _ = packed1.shape
     out = torch.empty((B, H, S, cb.d), dtype=torch.float16, device=packed1.device)
     kvq_rvq_unpack_decode(cb, packed1, packed2, norms, out, 0, stream)
+    return out
+
+
+def _check_stream(cb: Codebooks, name: str, t, B: int, H: int, S_cap: int) -> None:
+    shape = (B, H, S_cap, cb.n_words)
+    if tuple(t.shape) != shape or not t.is_contiguous() or t.element_size() != 4:
+        raise ValueError(f"{name} must be a contiguous 32-bit integer tensor of shape {shape}, got {tuple(t.shape)}")
+
+
+def kvq_mse_encode_pack(cb: Codebooks, x, packed, norms, s_offset: int = 0, stream=None) -> None:
+    """Single-stage encode. x: fp16 [B, H, S, d] contiguous; packed: int32/uint32
+    [B, H, S_cap, n_words]; norms: float32 [B, H, S_cap]."""
+    import torch
+    _require_cuda(x, packed, norms)
+    if x.dtype != torch.float16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, d = x.shape
+    if d != cb.d:
+        raise ValueError(f"x has d={d}, codebooks have d={cb.d}")
+    S_cap = packed.shape[2]
+    _check_stream(cb, "packed", packed, B, H, S_cap)
+    if tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32 or not norms.is_contiguous():
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    _check(load().kvq_mse_encode_pack(ctypes.byref(cb), _ptr(x), B, H, S, _ptr(packed), _ptr(norms), S_cap,
+                                      int(s_offset), _stream_handle(stream)), "kvq_mse_encode_pack")
+
+
+def kvq_mse_unpack_decode(cb: Codebooks, packed, norms, out, s_offset: int = 0, stream=None) -> None:
+    """Single-stage decode of cache positions [s_offset, s_offset + S) into out: fp16
+    [B, H, S, d]; norms=None gives unit reconstructions."""
+    import torch
+    _require_cuda(packed, norms, out)
+    if out.dtype != torch.float16 or out.dim() != 4 or not out.is_contiguous() or out.shape[3] != cb.d:
+        raise ValueError("out must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, _ = out.shape
+    S_cap = packed.shape[2]
+    _check_stream(cb, "packed", packed, B, H, S_cap)
+    if norms is not None and (tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32
+                              or not norms.is_contiguous()):
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    _check(load().kvq_mse_unpack_decode(ctypes.byref(cb), _ptr(packed), _ptr(norms), B, H, S_cap, int(s_offset), S,
+                                        _ptr(out), _stream_handle(stream)), "kvq_mse_unpack_decode")
+
+
+def encode_mse(x, cb: Codebooks, stream=None):
+    """Allocate outputs and run the single-stage encode. Returns (packed, norms)."""
+    import torch
+    B, H, S, d = x.shape
+    p = torch.empty((B, H, S, cb.n_words), dtype=torch.int32, device=x.device)
+    norms = torch.empty((B, H, S), dtype=torch.float32, device=x.device)
+    kvq_mse_encode_pack(cb, x, p, norms, 0, stream)
+    return p, norms
+
+
+def decode_mse(packed, norms, cb: Codebooks, stream=None):
+    """Allocate the output and run the single-stage decode. Returns fp16 [B, H, S, d]."""
+    import torch
+    B, H, S, _ = packed.shape
+    out = torch.empty((B, H, S, cb.d), dtype=torch.float16, device=packed.device)
+    kvq_mse_unpack_decode(cb, packed, norms, out, 0, stream)
     return out

@@ -10,8 +10,8 @@
 #include "params.h"
 
 namespace kvq {
-hipError_t launch_encode(const EncodeArgs& a, int d, int bits, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int d, int bits, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 }  // namespace kvq
 
 namespace {
@@ -151,15 +151,73 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
   return KVQ_OK;
 }
 
-void fill_decode_args(const kvq_codebooks* cb, DecodeArgs* a) {
+// stages = 2: entry (i1 << bits) | i2 is c1[i1] + c2[i2]; stages = 1: entry i1 << bits is c1[i1].
+void fill_decode_args(const kvq_codebooks* cb, int stages, DecodeArgs* a) {
   const int d = cb->d, bits = cb->bits, k = 1 << bits;
   a->inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
   std::memset(a->ztab, 0, sizeof(a->ztab));
-  for (int i1 = 0; i1 < k; ++i1)
-    for (int i2 = 0; i2 < k; ++i2) a->ztab[(i1 << bits) | i2] = cb->c1[i1] + cb->c2[i2];  // one float32 add
+  for (int i1 = 0; i1 < k; ++i1) {
+    if (stages == 1) {
+      a->ztab[i1 << bits] = cb->c1[i1];
+    } else {
+      for (int i2 = 0; i2 < k; ++i2) a->ztab[(i1 << bits) | i2] = cb->c1[i1] + cb->c2[i2];  // one float32 add
+    }
+  }
   std::memset(a->xmask, 0, sizeof(a->xmask));
   for (int m = 0; m < d / 2; ++m)
     a->xmask[m] = (sign_of(cb, 2 * m) < 0 ? 0x8000u : 0u) | (sign_of(cb, 2 * m + 1) < 0 ? 0x80000000u : 0u);
+}
+
+kvq_status encode_pack(const kvq_codebooks* cb, int stages, const uint16_t* x, int64_t B, int64_t H, int64_t S,
+                       uint32_t* packed1, uint32_t* packed2, float* norms, int64_t S_cap, int64_t s_offset,
+                       void* stream) {
+  kvq_status st = check_codebooks(cb);
+  if (st != KVQ_OK) return st;
+  int64_t n_vec = 0;
+  st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
+  if (st != KVQ_OK) return st;
+  if (n_vec == 0) return KVQ_OK;
+  if (x == nullptr || packed1 == nullptr || (stages == 2 && packed2 == nullptr) || norms == nullptr)
+    return KVQ_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(packed1, 16) || (stages == 2 && !aligned(packed2, 16)) || !aligned(norms, 4))
+    return KVQ_ERR_ALIGN;
+
+  EncodeArgs a;
+  a.x = x;
+  a.p1 = packed1;
+  a.p2 = stages == 2 ? packed2 : nullptr;
+  a.norms = norms;
+  a.n_vec = n_vec;
+  a.map = row_map(S, S_cap, s_offset);
+  st = fill_encode_args(cb, &a);
+  if (st != KVQ_OK) return st;
+  const hipError_t e = kvq::launch_encode(a, cb->d, cb->bits, stages, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+kvq_status unpack_decode(const kvq_codebooks* cb, int stages, const uint32_t* packed1, const uint32_t* packed2,
+                         const float* norms, int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
+                         uint16_t* x_out, void* stream) {
+  kvq_status st = check_codebooks(cb);
+  if (st != KVQ_OK) return st;
+  int64_t n_vec = 0;
+  st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
+  if (st != KVQ_OK) return st;
+  if (n_vec == 0) return KVQ_OK;
+  if (packed1 == nullptr || (stages == 2 && packed2 == nullptr) || x_out == nullptr) return KVQ_ERR_ARG;
+  if (!aligned(x_out, 16) || !aligned(packed1, 16) || (stages == 2 && !aligned(packed2, 16)) || !aligned(norms, 4))
+    return KVQ_ERR_ALIGN;
+
+  DecodeArgs a;
+  a.p1 = packed1;
+  a.p2 = stages == 2 ? packed2 : nullptr;
+  a.norms = norms;
+  a.x = x_out;
+  a.n_vec = n_vec;
+  a.map = row_map(S, S_cap, s_offset);
+  fill_decode_args(cb, stages, &a);
+  const hipError_t e = kvq::launch_decode(a, cb->d, cb->bits, stages, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
 }  // namespace
@@ -167,50 +225,24 @@ void fill_decode_args(const kvq_codebooks* cb, DecodeArgs* a) {
 extern "C" kvq_status kvq_rvq_encode_pack(const kvq_codebooks* cb, const uint16_t* x, int64_t B, int64_t H,
                                           int64_t S, uint32_t* packed1, uint32_t* packed2, float* norms,
                                           int64_t S_cap, int64_t s_offset, void* stream) {
-  kvq_status st = check_codebooks(cb);
-  if (st != KVQ_OK) return st;
-  int64_t n_vec = 0;
-  st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
-  if (st != KVQ_OK) return st;
-  if (n_vec == 0) return KVQ_OK;
-  if (x == nullptr || packed1 == nullptr || packed2 == nullptr || norms == nullptr) return KVQ_ERR_ARG;
-  if (!aligned(x, 16) || !aligned(packed1, 16) || !aligned(packed2, 16) || !aligned(norms, 4)) return KVQ_ERR_ALIGN;
-
-  EncodeArgs a;
-  a.x = x;
-  a.p1 = packed1;
-  a.p2 = packed2;
-  a.norms = norms;
-  a.n_vec = n_vec;
-  a.map = row_map(S, S_cap, s_offset);
-  st = fill_encode_args(cb, &a);
-  if (st != KVQ_OK) return st;
-  const hipError_t e = kvq::launch_encode(a, cb->d, cb->bits, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+  return encode_pack(cb, 2, x, B, H, S, packed1, packed2, norms, S_cap, s_offset, stream);
 }
 
 extern "C" kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed1,
                                             const uint32_t* packed2, const float* norms, int64_t B, int64_t H,
                                             int64_t S_cap, int64_t s_offset, int64_t S, uint16_t* x_out,
                                             void* stream) {
-  kvq_status st = check_codebooks(cb);
-  if (st != KVQ_OK) return st;
-  int64_t n_vec = 0;
-  st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
-  if (st != KVQ_OK) return st;
-  if (n_vec == 0) return KVQ_OK;
-  if (packed1 == nullptr || packed2 == nullptr || x_out == nullptr) return KVQ_ERR_ARG;
-  if (!aligned(x_out, 16) || !aligned(packed1, 16) || !aligned(packed2, 16) || !aligned(norms, 4))
-    return KVQ_ERR_ALIGN;
+  return unpack_decode(cb, 2, packed1, packed2, norms, B, H, S_cap, s_offset, S, x_out, stream);
+}
 
-  DecodeArgs a;
-  a.p1 = packed1;
-  a.p2 = packed2;
-  a.norms = norms;
-  a.x = x_out;
-  a.n_vec = n_vec;
-  a.map = row_map(S, S_cap, s_offset);
-  fill_decode_args(cb, &a);
-  const hipError_t e = kvq::launch_decode(a, cb->d, cb->bits, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+extern "C" kvq_status kvq_mse_encode_pack(const kvq_codebooks* cb, const uint16_t* x, int64_t B, int64_t H,
+                                          int64_t S, uint32_t* packed, float* norms, int64_t S_cap,
+                                          int64_t s_offset, void* stream) {
+  return encode_pack(cb, 1, x, B, H, S, packed, nullptr, norms, S_cap, s_offset, stream);
+}
+
+extern "C" kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed, const float* norms,
+                                            int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
+                                            uint16_t* x_out, void* stream) {
+  return unpack_decode(cb, 1, packed, nullptr, norms, B, H, S_cap, s_offset, S, x_out, stream);
 }

@@ -364,7 +364,10 @@ __device__ __forceinline__ void codes_bucket(float nx, float ay, float K2, int j
   *c2 = p2 ? HALF + m2 : HALF - 1u - m2;
 }
 
-template <int D, int BITS, bool CONTIG>
+// STAGES = 2: the two-stage residual codec (both code streams); STAGES = 1: the single-stage
+// codec ("turboquant" tag page, "Kernel 3": rotate, then the nearest Gaussian Lloyd-Max
+// centroid), stream 1 only.
+template <int D, int BITS, bool CONTIG, int STAGES>
 __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kernel(const EncodeArgs a) {
   using G = Layout<D>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
@@ -374,11 +377,12 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   constexpr int NWL = STAGED ? (NW + L - 1) / L : (L == 1 ? NW : C / EPW);  // words stored per lane
   constexpr int HALFM1 = (1 << (BITS - 1)) - 1;
   constexpr int CSTREAM = 64 * C / 4 + 4;            // STAGED: dwords per code stream (+ read pad)
+  constexpr bool TWO = STAGES == 2;                  // stage 2 computed and stored
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ float4 t1s[BITS >= 3 ? kTab1Max : 1];
   __shared__ float2 t2s[BITS >= 3 ? kTab2Max : 1];
-  __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? 2 * CSTREAM : 1];
+  __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? STAGES * CSTREAM : 1];
   if constexpr (BITS >= 3) {
     for (int i = threadIdx.x; i < kTab1Max; i += kBlockThreads)
       t1s[i] = make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3]);
@@ -471,12 +475,12 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
           const int w = q + L * k;
           if (w < NW) {
             __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + w);
-            __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
+            if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
           }
         }
       } else {
         store_words<NWL>(a.p1 + row_prev * NW + q * NWL, w1);
-        store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
+        if constexpr (TWO) store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
       }
     }
     {
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
           b2 = (b2 << 8) | c2;
         }
         cs[lane * (C / 4) + d4] = b1;
-        cs[CSTREAM + lane * (C / 4) + d4] = b2;
+        if constexpr (TWO) cs[CSTREAM + lane * (C / 4) + d4] = b2;
       }
       wave_lds_fence();
 #pragma unroll
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
         const int cnt = D - 10 * wc < 10 ? D - 10 * wc : 10;
         const uint32_t keep = cnt == 10 ? 0x3FFFFFFFu : (1u << (3 * cnt)) - 1u;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < STAGES; ++st) {
           const uint32_t* p = cs + st * CSTREAM + (base >> 2);
           const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
           const uint32_t e0 = __builtin_amdgcn_alignbit(d1, d0, s);
@@ -627,19 +631,21 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
         const int w = q + L * k;
         if (w < NW) {
           __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + w);
-          __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
+          if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
         }
       }
     } else {
       store_words<NWL>(a.p1 + row_prev * NW + q * NWL, w1);
-      store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
+      if constexpr (TWO) store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
     }
   }
 }
 
 // ------------------------------------------------------------------------------ decode
 
-template <int D, int BITS, bool CONTIG>
+// STAGES = 2: z = c1[i1] + c2[i2]; STAGES = 1: z = c1[i1] (the host fills the table so that
+// entry (i1 << BITS) holds the right value in both cases).
+template <int D, int BITS, bool CONTIG, int STAGES>
 __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kernel(const DecodeArgs a) {
   using G = Layout<D>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
@@ -650,11 +656,12 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   constexpr uint32_t MASK = (1u << BITS) - 1;
   constexpr int NZ = 1 << (2 * BITS);
   constexpr int CSTREAM = 64 * C / 4;  // STAGED: dwords per code stream
+  constexpr bool TWO = STAGES == 2;
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ uint4 smask[D / 8];
   __shared__ float zt[NZ];
-  __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? 2 * CSTREAM : 1];
+  __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? STAGES * CSTREAM : 1];
   for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
   for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   __syncthreads();
@@ -683,11 +690,16 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
       for (int k = 0; k < NWL; ++k) {
         const int w = q + L * k < NW ? q + L * k : NW - 1;
         nw1[k] = a.p1[row * NW + w];
-        nw2[k] = a.p2[row * NW + w];
+        nw2[k] = TWO ? a.p2[row * NW + w] : 0u;
       }
     } else {
       load_words<NWL>(a.p1 + row * NW + q * NWL, nw1);
-      load_words<NWL>(a.p2 + row * NW + q * NWL, nw2);
+      if constexpr (TWO) {
+        load_words<NWL>(a.p2 + row * NW + q * NWL, nw2);
+      } else {
+#pragma unroll
+        for (int k = 0; k < NWL; ++k) nw2[k] = 0u;
+      }
     }
     nnrm = a.norms ? a.norms[row] : 1.0f;
   };
@@ -733,7 +745,7 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
           const int base = vl * D + 10 * w;  // even
           const int cnt = D - 10 * w < 10 ? D - 10 * w : 10;  // even
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
+          for (int st = 0; st < STAGES; ++st) {
             const uint32_t wd = st == 0 ? w1[k] : w2[k];
             const uint32_t e0 = unpack4x3(wd), e1 = unpack4x3(wd >> 12), e2 = unpack4x3(wd >> 24);
             uint16_t* h = reinterpret_cast<uint16_t*>(cs + st * CSTREAM) + (base >> 1);
@@ -749,7 +761,7 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
       wave_lds_fence();
 #pragma unroll
       for (int d4 = 0; d4 < C / 4; ++d4) {
-        const uint32_t b1 = cs[lane * (C / 4) + d4], b2 = cs[CSTREAM + lane * (C / 4) + d4];
+        const uint32_t b1 = cs[lane * (C / 4) + d4], b2 = TWO ? cs[CSTREAM + lane * (C / 4) + d4] : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t i1 = (b1 >> (8 * i)) & MASK, i2 = (b2 >> (8 * i)) & MASK;
@@ -821,62 +833,70 @@ static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* 
   return hipLaunchKernel(f, dim3(blocks), dim3(kBlockThreads), a, 0, stream);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int STAGES>
 static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   static int cap[2] = {0, 0};
   const bool c = a.map.contiguous != 0;
-  const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true>)
-                    : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false>);
+  const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES>)
+                    : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES>);
   return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, &cap[c ? 1 : 0], stream);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int STAGES>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   static int cap[2] = {0, 0};
   const bool c = a.map.contiguous != 0;
-  const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true>)
-                    : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false>);
+  const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES>)
+                    : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES>);
   return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, &cap[c ? 1 : 0], stream);
 }
 
-#define KVQ_FOR_BITS(MACRO, D) \
-  case 1: return MACRO<D, 1>; case 2: return MACRO<D, 2>; case 3: return MACRO<D, 3>; case 4: return MACRO<D, 4>;
+#define KVQ_FOR_BITS(MACRO, D, S) \
+  case 1: return MACRO<D, 1, S>; case 2: return MACRO<D, 2, S>; case 3: return MACRO<D, 3, S>; case 4: return MACRO<D, 4, S>;
 
 template <int D>
-static auto encode_fn(int bits) -> hipError_t (*)(const EncodeArgs&, hipStream_t) {
-  switch (bits) { KVQ_FOR_BITS(launch_encode_t, D) }
+static auto encode_fn(int bits, int stages) -> hipError_t (*)(const EncodeArgs&, hipStream_t) {
+  if (stages == 2) {
+    switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 2) }
+  } else if (stages == 1) {
+    switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 1) }
+  }
   return nullptr;
 }
 template <int D>
-static auto decode_fn(int bits) -> hipError_t (*)(const DecodeArgs&, hipStream_t) {
-  switch (bits) { KVQ_FOR_BITS(launch_decode_t, D) }
+static auto decode_fn(int bits, int stages) -> hipError_t (*)(const DecodeArgs&, hipStream_t) {
+  if (stages == 2) {
+    switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 2) }
+  } else if (stages == 1) {
+    switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 1) }
+  }
   return nullptr;
 }
 
-#define KVQ_FOR_D(FN, bits)               \
-  switch (d) {                            \
-    case 8: f = FN<8>(bits); break;       \
-    case 16: f = FN<16>(bits); break;     \
-    case 32: f = FN<32>(bits); break;     \
-    case 64: f = FN<64>(bits); break;     \
-    case 128: f = FN<128>(bits); break;   \
-    case 256: f = FN<256>(bits); break;   \
-    case 512: f = FN<512>(bits); break;   \
-    case 1024: f = FN<1024>(bits); break; \
-    default: break;                       \
+#define KVQ_FOR_D(FN, bits, stages)               \
+  switch (d) {                                    \
+    case 8: f = FN<8>(bits, stages); break;       \
+    case 16: f = FN<16>(bits, stages); break;     \
+    case 32: f = FN<32>(bits, stages); break;     \
+    case 64: f = FN<64>(bits, stages); break;     \
+    case 128: f = FN<128>(bits, stages); break;   \
+    case 256: f = FN<256>(bits, stages); break;   \
+    case 512: f = FN<512>(bits, stages); break;   \
+    case 1024: f = FN<1024>(bits, stages); break; \
+    default: break;                               \
   }
 
-// Launchers used by api.cpp. Return hipErrorInvalidValue for an unsupported (d, bits) or
-// more than 2^31 - 1 tiles.
-hipError_t launch_encode(const EncodeArgs& a, int d, int bits, hipStream_t stream) {
+// Launchers used by api.cpp. Return hipErrorInvalidValue for an unsupported (d, bits,
+// stages) or more than 2^31 - 1 tiles.
+hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream) {
   hipError_t (*f)(const EncodeArgs&, hipStream_t) = nullptr;
-  KVQ_FOR_D(encode_fn, bits)
+  KVQ_FOR_D(encode_fn, bits, stages)
   return f ? f(a, stream) : hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int d, int bits, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream) {
   hipError_t (*f)(const DecodeArgs&, hipStream_t) = nullptr;
-  KVQ_FOR_D(decode_fn, bits)
+  KVQ_FOR_D(decode_fn, bits, stages)
   return f ? f(a, stream) : hipErrorInvalidValue;
 }
 

@@ -117,3 +117,48 @@ def check_decode_from_oracle_words(ref: dict, signs, bits, shape, with_norms=Tru
         err_rel = float(np.max(np.abs(got - want) / np.maximum(n, 1e-30))) if got.size else 0.0
         assert not got.size or float(np.max(excess)) <= 0.0, err_rel
     return err_unit, err_rel
+
+
+# ----------------------------------------------------------------- single-stage codec
+
+def check_encode_mse(x: torch.Tensor, signs, bits, max_flip=None, S_cap=None, s_offset=0):
+    """Single-stage encode on the GPU against the oracle's encode_mse under the same rule."""
+    B, H, S, D = x.shape
+    S_cap = S if S_cap is None else S_cap
+    cb = kvq.build_codebooks(D, bits, signs)
+    p = torch.full((B, H, S_cap, cb.n_words), -1, dtype=torch.int32, device=x.device)
+    nrm = torch.full((B, H, S_cap), float("nan"), dtype=torch.float32, device=x.device)
+    kvq.kvq_mse_encode_pack(cb, x, p, nrm, s_offset)
+    torch.cuda.synchronize()
+    t = tables(D, bits)
+    ref = rvq.encode_mse(x.detach().cpu().numpy().reshape(-1, D), np.asarray(signs, np.int8), t)
+    win_p = as_u32(p[:, :, s_offset:s_offset + S]).reshape(-1, cb.n_words)
+    win_n = nrm[:, :, s_offset:s_offset + S].cpu().numpy().reshape(-1)
+    rep = flips.compare_encode_single(win_p, win_n, ref, t, REL_WINDOW)
+    cap = flip_cap(rep.n_codes) if max_flip is None else max_flip
+    assert rep.ok(cap, NORM_REL_TOL), rep.summary()
+    return rep, (p, nrm), ref
+
+
+def check_decode_mse_from_oracle_words(ref: dict, signs, bits, shape):
+    """Feed the oracle's single-stage words to the GPU decoder and to the oracle decoder."""
+    B, H, S, D = shape
+    t = tables(D, bits)
+    cb = kvq.build_codebooks(D, bits, signs)
+    dev = torch.device("cuda")
+    p = torch.from_numpy(ref["packed"].view(np.int32)).reshape(B, H, S, -1).to(dev)
+    out = torch.empty((B, H, S, D), dtype=torch.float16, device=dev)
+    kvq.kvq_mse_unpack_decode(cb, p, None, out)
+    torch.cuda.synchronize()
+    got = _finite16(out.cpu().numpy().reshape(-1, D))
+    want = _finite16(rvq.decode_mse(ref["packed"], None, np.asarray(signs), t))
+    err_unit = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err_unit <= DECODE_UNIT_ATOL, err_unit
+    nrm = torch.from_numpy(ref["norms"]).reshape(B, H, S).to(dev)
+    kvq.kvq_mse_unpack_decode(cb, p, nrm, out)
+    torch.cuda.synchronize()
+    got = _finite16(out.cpu().numpy().reshape(-1, D))
+    want = _finite16(rvq.decode_mse(ref["packed"], ref["norms"], np.asarray(signs), t))
+    n = ref["norms"].astype(np.float64)[:, None]
+    assert not got.size or float(np.max(np.abs(got - want) - (DECODE_UNIT_ATOL * n + 2.0 ** -24))) <= 0.0
+    return err_unit

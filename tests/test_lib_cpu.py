@@ -27,7 +27,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = kvq.load()
     names = _declared_functions()
-    assert names == ["kvq_build_codebooks", "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str"]
+    assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_rvq_encode_pack",
+                     "kvq_rvq_unpack_decode", "kvq_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.library_path()], capture_output=True, text=True).stdout
@@ -124,6 +125,28 @@ def test_host_side_argument_checks():
     assert _dec(pcb, A, A, None, 1, 1, 4, 0, 4, A + 2) == -3
     assert _dec(pcb, None, A, None, 1, 1, 4, 0, 4, A) == -1
     assert _dec(pcb, A, A, None, 1, 1, 4, 2, 4, A) == -4
+
+
+def test_single_stage_host_side_argument_checks():
+    """The single-stage entry points share the checks; the second stream is not needed."""
+    lib = kvq.load()
+    cb = kvq.build_codebooks(128, 2)
+    pcb = ctypes.byref(cb)
+    A = 0x10000
+    enc = lambda *a: lib.kvq_mse_encode_pack(*a, None)
+    dec = lambda *a: lib.kvq_mse_unpack_decode(*a, None)
+    assert enc(None, A, 1, 1, 1, A, A, 1, 0) == -1
+    assert enc(pcb, A, 1, 1, 5, A, A, 4, 0) == -4
+    assert enc(pcb, None, 0, 3, 3, None, None, 3, 0) == 0
+    assert enc(pcb, None, 1, 1, 1, A, A, 1, 0) == -1
+    assert enc(pcb, A, 1, 1, 1, None, A, 1, 0) == -1
+    assert enc(pcb, A, 1, 1, 1, A, None, 1, 0) == -1
+    assert enc(pcb, A, 1, 1, 1, A + 4, A, 1, 0) == -3
+    assert enc(pcb, A + 2, 1, 1, 1, A, A, 1, 0) == -3
+    assert dec(pcb, None, None, 1, 1, 4, 0, 4, A) == -1
+    assert dec(pcb, A, None, 1, 1, 4, 0, 4, A + 2) == -3
+    assert dec(pcb, A, None, 1, 1, 4, 2, 4, A) == -4
+    assert dec(pcb, None, None, 0, 1, 4, 0, 4, None) == 0
 
 
 def test_python_binding_rejects_cpu_tensors():
