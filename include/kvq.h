@@ -157,6 +157,49 @@ kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed
                                  int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
                                  uint16_t* x_out, void* stream);
 
+/*
+ * kvq_rvq_attend - device. Softmax attention of fp16 queries over a packed two-stage key
+ * cache and value cache, without reconstructing either (blog, "turboquant" tag page,
+ * "Kernel 5": keys decoded as c1[i1] + c2[i2] on the fly inside a FlashAttention-style
+ * online softmax). For every query vector (b, h, s):
+ *     out = sum_t p_t vhat_t,   p = softmax_t(scale * q . khat_t),   t in [0, S_kv)
+ * where khat_t and vhat_t are the float32 reconstructions n_t diag(s) H z_t / sqrt(d) that
+ * kvq_rvq_unpack_decode would round to fp16 (no rounding is applied to them here). Every
+ * query attends to all S_kv cached positions (no mask). The work runs in the rotated
+ * domain: q . khat_t = n_t (R q) . z_t, and the weighted sum of values is rotated back once.
+ *   cbk, cbv     codebooks of the key and of the value cache (same d and bits; the sign
+ *                vectors may differ)
+ *   q            device fp16 [B, Hq, Sq, d], contiguous, 16-byte aligned
+ *   Hkv          key/value heads; Hq must be a multiple of Hkv (query head h reads
+ *                key/value head h / (Hq / Hkv))
+ *   k_packed1/2, k_norms, v_packed1/2, v_norms
+ *                caches written by kvq_rvq_encode_pack: [B, Hkv, S_cap, n_words] and
+ *                [B, Hkv, S_cap]; positions [0, S_kv) are read
+ *   S_cap, S_kv  cache capacity and valid length, 1 <= S_kv <= S_cap
+ *   scale        softmax scale (finite; 1/sqrt(d) for standard attention)
+ *   workspace    device scratch of at least kvq_rvq_attend_workspace_size bytes, 16-byte
+ *                aligned, owned by the caller; its contents are overwritten
+ *   out          device fp16 [B, Hq, Sq, d], contiguous, 16-byte aligned
+ * Errors: KVQ_ERR_ARG (null pointer, non-finite scale, inconsistent codebooks),
+ * KVQ_ERR_SHAPE (codebooks of different d or bits, negative sizes, Hq not a multiple of
+ * Hkv), KVQ_ERR_ALIGN, KVQ_ERR_RANGE (S_kv out of range, workspace too small, overflow),
+ * KVQ_ERR_DEVICE. B * Hq * Sq == 0 returns KVQ_OK without touching any pointer.
+ */
+kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
+                          int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
+                          const uint32_t* k_packed1, const uint32_t* k_packed2, const float* k_norms,
+                          const uint32_t* v_packed1, const uint32_t* v_packed2, const float* v_norms,
+                          int64_t S_cap, int64_t S_kv, float scale,
+                          void* workspace, int64_t workspace_bytes, uint16_t* out, void* stream);
+
+/*
+ * kvq_rvq_attend_workspace_size - host. Workspace bytes kvq_rvq_attend needs for these
+ * sizes (d as in the codebooks). Errors: KVQ_ERR_ARG (bytes NULL), KVQ_ERR_SHAPE,
+ * KVQ_ERR_RANGE (S_kv < 1 or overflow).
+ */
+kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_kv,
+                                         int64_t* bytes);
+
 /* Static text for a status code; never NULL. */
 const char* kvq_status_str(kvq_status status);
 

@@ -22,4 +22,5 @@ Modules:
   rvq        encode (normalize, rotate, quantize twice, pack) and decode.
   packing    LSB-first b-bit packing into uint32 words and its inverse.
   flips      the comparison rule between a device result and the oracle.
+  attend     softmax attention over packed key/value caches (the plain definition).
 """

@@ -24,7 +24,8 @@ from typing import Optional
 __all__ = [
     "KvqError", "Codebooks", "load", "library_path", "build_codebooks", "kvq_build_codebooks",
     "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_mse_encode_pack", "kvq_mse_unpack_decode",
-    "kvq_status_str", "encode", "decode", "encode_mse", "decode_mse", "n_words",
+    "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_status_str", "encode", "decode", "encode_mse",
+    "decode_mse", "attend", "n_words",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,11 @@ def load() -> ctypes.CDLL:
     lib.kvq_mse_encode_pack.restype = ctypes.c_int
     lib.kvq_mse_unpack_decode.argtypes = [ctypes.POINTER(Codebooks), ptr, ptr, i64, i64, i64, i64, i64, ptr, ptr]
     lib.kvq_mse_unpack_decode.restype = ctypes.c_int
+    lib.kvq_rvq_attend.argtypes = [ctypes.POINTER(Codebooks), ctypes.POINTER(Codebooks), ptr, i64, i64, i64, i64,
+                                   ptr, ptr, ptr, ptr, ptr, ptr, i64, i64, ctypes.c_float, ptr, i64, ptr, ptr]
+    lib.kvq_rvq_attend.restype = ctypes.c_int
+    lib.kvq_rvq_attend_workspace_size.argtypes = [ctypes.c_int32, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.kvq_rvq_attend_workspace_size.restype = ctypes.c_int
     lib.kvq_status_str.argtypes = [ctypes.c_int]
     lib.kvq_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -267,4 +273,51 @@ def decode_mse(packed, norms, cb: Codebooks, stream=None):
     B, H, S, _ = packed.shape
     out = torch.empty((B, H, S, cb.d), dtype=torch.float16, device=packed.device)
     kvq_mse_unpack_decode(cb, packed, norms, out, 0, stream)
+    return out
+
+
+def kvq_rvq_attend_workspace_size(d: int, B: int, Hq: int, Sq: int, S_kv: int) -> int:
+    """Workspace bytes kvq_rvq_attend needs (host call)."""
+    out = ctypes.c_int64(0)
+    _check(load().kvq_rvq_attend_workspace_size(int(d), int(B), int(Hq), int(Sq), int(S_kv), ctypes.byref(out)),
+           "kvq_rvq_attend_workspace_size")
+    return out.value
+
+
+def kvq_rvq_attend(cbk: Codebooks, cbv: Codebooks, q, kcache, vcache, S_kv: int, scale: float, workspace, out,
+                   stream=None) -> None:
+    """Attention of q (fp16 [B, Hq, Sq, d]) over cached positions [0, S_kv) of packed caches
+    kcache = (packed1, packed2, norms) and vcache (the same), each [B, Hkv, S_cap, n_words] /
+    [B, Hkv, S_cap]. workspace: a device tensor of at least kvq_rvq_attend_workspace_size
+    bytes; out: fp16 [B, Hq, Sq, d]."""
+    import torch
+    k1, k2, kn = kcache
+    v1, v2, vn = vcache
+    _require_cuda(q, k1, k2, kn, v1, v2, vn, workspace, out)
+    if q.dtype != torch.float16 or q.dim() != 4 or not q.is_contiguous() or q.shape[3] != cbk.d:
+        raise ValueError("q must be a contiguous fp16 [B, Hq, Sq, d] tensor")
+    if out.dtype != torch.float16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q")
+    B, Hq, Sq, _ = q.shape
+    Hkv, S_cap = k1.shape[1], k1.shape[2]
+    for name, t in (("k_packed1", k1), ("k_packed2", k2), ("v_packed1", v1), ("v_packed2", v2)):
+        _check_stream(cbk, name, t, B, Hkv, S_cap)
+    for name, t in (("k_norms", kn), ("v_norms", vn)):
+        if tuple(t.shape) != (B, Hkv, S_cap) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 {(B, Hkv, S_cap)}")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().kvq_rvq_attend(ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q), B, Hq, Sq, Hkv, _ptr(k1), _ptr(k2),
+                                 _ptr(kn), _ptr(v1), _ptr(v2), _ptr(vn), S_cap, int(S_kv), float(scale),
+                                 _ptr(workspace), nbytes, _ptr(out), _stream_handle(stream)), "kvq_rvq_attend")
+
+
+def attend(q, kcache, vcache, cbk: Codebooks, cbv: Codebooks, S_kv: int, scale=None, stream=None):
+    """Allocate the workspace and output and run kvq_rvq_attend. scale defaults to 1/sqrt(d)."""
+    import math
+    import torch
+    B, Hq, Sq, d = q.shape
+    ws = torch.empty(max(16, kvq_rvq_attend_workspace_size(d, B, Hq, Sq, S_kv)) // 4, dtype=torch.float32,
+                     device=q.device)
+    out = torch.empty_like(q)
+    kvq_rvq_attend(cbk, cbv, q, kcache, vcache, S_kv, 1.0 / math.sqrt(d) if scale is None else scale, ws, out, stream)
     return out

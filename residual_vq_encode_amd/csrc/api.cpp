@@ -12,10 +12,12 @@
 namespace kvq {
 hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
+hipError_t launch_attend(const AttendArgs& a, int d, int bits, hipStream_t stream);
 }  // namespace kvq
 
 namespace {
 
+using kvq::AttendArgs;
 using kvq::DecodeArgs;
 using kvq::EncodeArgs;
 using kvq::RowMap;
@@ -245,4 +247,124 @@ extern "C" kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint3
                                             int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
                                             uint16_t* x_out, void* stream) {
   return unpack_decode(cb, 1, packed, nullptr, norms, B, H, S_cap, s_offset, S, x_out, stream);
+}
+
+// ------------------------------------------------------------------------------ attention
+
+namespace {
+
+// How the attention splits the cached positions: chunks of a multiple of the lane layout's
+// positions per wave iteration, enough of them that the partial pass has about 8192 wave
+// units, but at least 8 iterations per chunk.
+struct AttendPlan {
+  int64_t n_q = 0;
+  int32_t chunk = 0, n_splits = 0;
+  int64_t ws_bytes = 0;
+};
+
+kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_kv, AttendPlan* p) {
+  if (d < KVQ_MIN_D || d > KVQ_MAX_D || !is_pow2(d)) return KVQ_ERR_SHAPE;
+  if (B < 0 || Hq < 0 || Sq < 0) return KVQ_ERR_SHAPE;
+  if (S_kv < 1 || S_kv > (int64_t(1) << 40)) return KVQ_ERR_RANGE;
+  int64_t bh = 0, n_q = 0;
+  if (!mul_ok(B, Hq, &bh) || !mul_ok(bh, Sq, &n_q)) return KVQ_ERR_RANGE;
+  const int64_t c = d < 32 ? d : 32, vw = 64 / (d / c);
+  const int64_t want_units = 8192;
+  const int64_t splits0 = n_q > 0 ? (want_units + n_q - 1) / n_q : 1;
+  int64_t chunk = (S_kv + splits0 - 1) / splits0;
+  chunk = (chunk + vw - 1) / vw * vw;
+  if (chunk < 8 * vw) chunk = 8 * vw;
+  if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;
+  const int64_t n_splits = (S_kv + chunk - 1) / chunk;
+  int64_t units = 0, ws = 0;
+  if (!mul_ok(n_q, n_splits, &units) || !mul_ok(units, (d + 4) * 4, &ws)) return KVQ_ERR_RANGE;
+  if (units / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max()) return KVQ_ERR_RANGE;
+  p->n_q = n_q;
+  p->chunk = static_cast<int32_t>(chunk);
+  p->n_splits = static_cast<int32_t>(n_splits);
+  p->ws_bytes = ws;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_kv,
+                                                    int64_t* bytes) {
+  if (bytes == nullptr) return KVQ_ERR_ARG;
+  AttendPlan p;
+  const kvq_status st = attend_plan(d, B, Hq, Sq, S_kv, &p);
+  if (st != KVQ_OK) return st;
+  *bytes = p.ws_bytes;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
+                                     int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, const uint32_t* k_packed1,
+                                     const uint32_t* k_packed2, const float* k_norms, const uint32_t* v_packed1,
+                                     const uint32_t* v_packed2, const float* v_norms, int64_t S_cap, int64_t S_kv,
+                                     float scale, void* workspace, int64_t workspace_bytes, uint16_t* out,
+                                     void* stream) {
+  kvq_status st = check_codebooks(cbk);
+  if (st != KVQ_OK) return st;
+  st = check_codebooks(cbv);
+  if (st != KVQ_OK) return st;
+  if (cbk->d != cbv->d || cbk->bits != cbv->bits) return KVQ_ERR_SHAPE;
+  if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 0) return KVQ_ERR_SHAPE;
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return KVQ_ERR_SHAPE;
+  if (Hkv > std::numeric_limits<int32_t>::max() || Sq > std::numeric_limits<int32_t>::max() ||
+      (Hkv > 0 && Hq / Hkv > std::numeric_limits<int32_t>::max()))
+    return KVQ_ERR_RANGE;
+  if (S_kv < 1 || S_cap < S_kv) return KVQ_ERR_RANGE;
+  AttendPlan p;
+  st = attend_plan(cbk->d, B, Hq, Sq, S_kv, &p);
+  if (st != KVQ_OK) return st;
+  // the caches: [B, Hkv, S_cap, n_words] words and [B, Hkv, S_cap] norms must be addressable
+  int64_t rows = 0, words = 0, bytes = 0;
+  if (!mul_ok(B, Hkv, &rows) || !mul_ok(rows, S_cap, &rows) || !mul_ok(rows, cbk->n_words, &words) ||
+      !mul_ok(words, 4, &bytes))
+    return KVQ_ERR_RANGE;
+  if (p.n_q == 0) return KVQ_OK;
+  if (!std::isfinite(scale)) return KVQ_ERR_ARG;
+  if (q == nullptr || k_packed1 == nullptr || k_packed2 == nullptr || k_norms == nullptr || v_packed1 == nullptr ||
+      v_packed2 == nullptr || v_norms == nullptr || workspace == nullptr || out == nullptr)
+    return KVQ_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 16) || !aligned(k_packed1, 16) ||
+      !aligned(k_packed2, 16) || !aligned(v_packed1, 16) || !aligned(v_packed2, 16) || !aligned(k_norms, 4) ||
+      !aligned(v_norms, 4))
+    return KVQ_ERR_ALIGN;
+  if (workspace_bytes < p.ws_bytes) return KVQ_ERR_RANGE;
+
+  AttendArgs a;
+  a.q = q;
+  a.k1 = k_packed1;
+  a.k2 = k_packed2;
+  a.kn = k_norms;
+  a.v1 = v_packed1;
+  a.v2 = v_packed2;
+  a.vn = v_norms;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.n_q = p.n_q;
+  a.S_cap = S_cap;
+  a.S_kv = S_kv;
+  a.Hkv = static_cast<int32_t>(Hkv);
+  a.group = static_cast<int32_t>(Hq / Hkv);
+  a.Sq = static_cast<int32_t>(Sq);
+  a.chunk = p.chunk;
+  a.n_splits = p.n_splits;
+  const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(cbk->d));
+  a.qscale = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634 * inv_sqrt_d);  // log2(e)
+  a.inv_sqrt_d = static_cast<float>(inv_sqrt_d);
+  const int k = 1 << cbk->bits;
+  std::memset(a.ztab_k, 0, sizeof(a.ztab_k));
+  std::memset(a.ztab_v, 0, sizeof(a.ztab_v));
+  for (int i1 = 0; i1 < k; ++i1)
+    for (int i2 = 0; i2 < k; ++i2) {
+      a.ztab_k[(i1 << cbk->bits) | i2] = cbk->c1[i1] + cbk->c2[i2];  // one float32 add
+      a.ztab_v[(i1 << cbv->bits) | i2] = cbv->c1[i1] + cbv->c2[i2];
+    }
+  std::memcpy(a.ksign, cbk->sign_bits, sizeof(a.ksign));
+  std::memcpy(a.vsign, cbv->sign_bits, sizeof(a.vsign));
+  const hipError_t e = kvq::launch_attend(a, cbk->d, cbk->bits, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }

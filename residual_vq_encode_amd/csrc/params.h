@@ -61,3 +61,31 @@ struct DecodeArgs {
 };
 
 }  // namespace kvq
+
+namespace kvq {
+
+// Attention over a packed cache (attend.hip): scores of the query against every cached key
+// and the softmax-weighted sum of the cached values, both caches read packed.
+struct AttendArgs {
+  const uint16_t* q;                // fp16 [B, Hq, Sq, d]
+  const uint32_t* k1;               // key cache streams [B, Hkv, S_cap, n_words]
+  const uint32_t* k2;
+  const float* kn;                  // key norms [B, Hkv, S_cap]
+  const uint32_t* v1;               // value cache streams
+  const uint32_t* v2;
+  const float* vn;
+  float* ws;                        // per (query vector, split): {m, l, 0, 0, acc[d]}
+  uint16_t* out;                    // fp16 [B, Hq, Sq, d]
+  int64_t n_q;                      // B * Hq * Sq query vectors
+  int64_t S_cap, S_kv;
+  int32_t Hkv, group, Sq;           // group = Hq / Hkv query heads per key/value head
+  int32_t chunk, n_splits;          // keys per split, splits per query vector
+  float qscale;                     // scale * log2(e) / sqrt(d): scores come out in base-2 units
+  float inv_sqrt_d;
+  float ztab_k[256];                // c1[i1] + c2[i2] of the key codebooks, index (i1 << bits) | i2
+  float ztab_v[256];                // the same for the value codebooks
+  uint32_t ksign[32];               // bit j: the key rotation negates coordinate j
+  uint32_t vsign[32];               // the same for the values
+};
+
+}  // namespace kvq

@@ -27,8 +27,9 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = kvq.load()
     names = _declared_functions()
-    assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_rvq_encode_pack",
-                     "kvq_rvq_unpack_decode", "kvq_status_str"]
+    assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_rvq_attend",
+                     "kvq_rvq_attend_workspace_size", "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode",
+                     "kvq_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.library_path()], capture_output=True, text=True).stdout
@@ -147,6 +148,47 @@ def test_single_stage_host_side_argument_checks():
     assert dec(pcb, A, None, 1, 1, 4, 0, 4, A + 2) == -3
     assert dec(pcb, A, None, 1, 1, 4, 2, 4, A) == -4
     assert dec(pcb, None, None, 0, 1, 4, 0, 4, None) == 0
+
+
+def test_attend_host_side_argument_checks():
+    """Every rejection happens on the host; the workspace size follows the documented plan."""
+    lib = kvq.load()
+    cb = kvq.build_codebooks(128, 2)
+    cb4 = kvq.build_codebooks(128, 4)
+    cb64 = kvq.build_codebooks(64, 2)
+    A = 0x10000
+    P = ctypes.byref
+
+    def att(cbk=cb, cbv=cb, q=A, B=1, Hq=4, Sq=1, Hkv=2, ptrs=(A, A, A, A, A, A), S_cap=100, S_kv=50, scale=0.1,
+            ws=A, wsb=1 << 30, out=A):
+        return lib.kvq_rvq_attend(P(cbk) if cbk is not None else None, P(cbv) if cbv is not None else None, q, B, Hq,
+                                  Sq, Hkv, *ptrs, S_cap, S_kv, scale, ws, wsb, out, None)
+
+    assert att(cbk=None) == -1
+    assert att(cbv=cb4) == -2 and att(cbv=cb64) == -2
+    assert att(Hq=3) == -2 and att(Hkv=0) == -2 and att(B=-1) == -2
+    assert att(S_kv=0) == -4 and att(S_kv=101) == -4
+    assert att(B=0) == 0 and att(Hq=0, Hkv=0) == 0 and att(Sq=0) == 0
+    assert att(scale=float("inf")) == -1 and att(scale=float("nan")) == -1
+    assert att(q=None) == -1 and att(ws=None) == -1 and att(out=None) == -1
+    assert att(ptrs=(A, A, None, A, A, A)) == -1
+    assert att(q=A + 2) == -3 and att(out=A + 8) == -3 and att(ws=A + 4) == -3
+    assert att(ptrs=(A + 4, A, A, A, A, A)) == -3 and att(ptrs=(A, A, A + 2, A, A, A)) == -3
+    need = kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 50)
+    assert need > 0 and att(wsb=need - 1) == -4
+    assert lib.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 50, None) == -1
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_rvq_attend_workspace_size(96, 1, 4, 1, 50)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 0)
+    # plan: chunks of whole 16-position iterations, about 8192 wave units, at least 8 iterations each
+    for (B, Hq, Sq, S_kv) in ((1, 32, 1, 32768), (1, 1, 1, 5), (4, 8, 3, 1000), (1, 32, 1, 1)):
+        nq = B * Hq * Sq
+        splits0 = -(-8192 // nq)
+        chunk = -(-S_kv // splits0)
+        chunk = max(-(-chunk // 16) * 16, 128)
+        n_splits = -(-S_kv // chunk)
+        assert kvq.kvq_rvq_attend_workspace_size(128, B, Hq, Sq, S_kv) == nq * n_splits * (128 + 4) * 4
 
 
 def test_python_binding_rejects_cpu_tensors():
