@@ -12,7 +12,7 @@
 namespace kvq {
 hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
-hipError_t launch_attend(const AttendArgs& a, int d, int bits, hipStream_t stream);
+hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream);
 }  // namespace kvq
 
 namespace {
@@ -253,24 +253,33 @@ extern "C" kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint3
 
 namespace {
 
-// How the attention splits the cached positions: chunks of a multiple of the lane layout's
-// positions per wave iteration, enough of them that the partial pass has about 8192 wave
-// units, but at least 8 iterations per chunk.
+// How the attention splits its work. A wave serves nqw query vectors that read the same
+// key/value head (the largest of 4, 2, 1 that divides the query vectors per head; 1 at
+// d = 1024, where their state does not fit the registers). The cached positions are cut into
+// chunks of a multiple of the lane layout's positions per wave iteration, enough of them that
+// the partial pass has about 2048 waves (several per SIMD; longer chunks amortise each wave's
+// query rotation and its final merge, and leave fewer partial results to combine), but at
+// least 8 iterations per chunk.
 struct AttendPlan {
   int64_t n_q = 0;
-  int32_t chunk = 0, n_splits = 0;
+  int32_t chunk = 0, n_splits = 0, nqw = 1;
   int64_t ws_bytes = 0;
 };
 
-kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_kv, AttendPlan* p) {
+kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, int64_t S_kv, AttendPlan* p) {
   if (d < KVQ_MIN_D || d > KVQ_MAX_D || !is_pow2(d)) return KVQ_ERR_SHAPE;
-  if (B < 0 || Hq < 0 || Sq < 0) return KVQ_ERR_SHAPE;
+  if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 0) return KVQ_ERR_SHAPE;
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return KVQ_ERR_SHAPE;
   if (S_kv < 1 || S_kv > (int64_t(1) << 40)) return KVQ_ERR_RANGE;
-  int64_t bh = 0, n_q = 0;
+  int64_t bh = 0, n_q = 0, gq = 0;
   if (!mul_ok(B, Hq, &bh) || !mul_ok(bh, Sq, &n_q)) return KVQ_ERR_RANGE;
-  const int64_t c = d < 32 ? d : 32, vw = 64 / (d / c);
-  const int64_t want_units = 8192;
-  const int64_t splits0 = n_q > 0 ? (want_units + n_q - 1) / n_q : 1;
+  if (Hq > 0 && !mul_ok(Hq / Hkv, Sq, &gq)) return KVQ_ERR_RANGE;
+  int nqw = 1;
+  if (d <= 512) nqw = gq % 4 == 0 ? 4 : gq % 2 == 0 ? 2 : 1;
+  const int64_t cm = (nqw > 1 && d >= 32) ? 16 : 32;  // coordinates per lane
+  const int64_t c = d < cm ? d : cm, vw = 64 / (d / c);
+  const int64_t want_waves = 2048;
+  const int64_t splits0 = n_q > 0 ? (want_waves * nqw + n_q - 1) / n_q : 1;
   int64_t chunk = (S_kv + splits0 - 1) / splits0;
   chunk = (chunk + vw - 1) / vw * vw;
   if (chunk < 8 * vw) chunk = 8 * vw;
@@ -278,21 +287,24 @@ kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_k
   const int64_t n_splits = (S_kv + chunk - 1) / chunk;
   int64_t units = 0, ws = 0;
   if (!mul_ok(n_q, n_splits, &units) || !mul_ok(units, (d + 4) * 4, &ws)) return KVQ_ERR_RANGE;
-  if (units / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max()) return KVQ_ERR_RANGE;
+  if (units / nqw / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max() ||
+      n_q > std::numeric_limits<int32_t>::max())
+    return KVQ_ERR_RANGE;
   p->n_q = n_q;
   p->chunk = static_cast<int32_t>(chunk);
   p->n_splits = static_cast<int32_t>(n_splits);
+  p->nqw = nqw;
   p->ws_bytes = ws;
   return KVQ_OK;
 }
 
 }  // namespace
 
-extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t S_kv,
-                                                    int64_t* bytes) {
+extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
+                                                    int64_t S_kv, int64_t* bytes) {
   if (bytes == nullptr) return KVQ_ERR_ARG;
   AttendPlan p;
-  const kvq_status st = attend_plan(d, B, Hq, Sq, S_kv, &p);
+  const kvq_status st = attend_plan(d, B, Hq, Sq, Hkv, S_kv, &p);
   if (st != KVQ_OK) return st;
   *bytes = p.ws_bytes;
   return KVQ_OK;
@@ -316,7 +328,7 @@ extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codeboo
     return KVQ_ERR_RANGE;
   if (S_kv < 1 || S_cap < S_kv) return KVQ_ERR_RANGE;
   AttendPlan p;
-  st = attend_plan(cbk->d, B, Hq, Sq, S_kv, &p);
+  st = attend_plan(cbk->d, B, Hq, Sq, Hkv, S_kv, &p);
   if (st != KVQ_OK) return st;
   // the caches: [B, Hkv, S_cap, n_words] words and [B, Hkv, S_cap] norms must be addressable
   int64_t rows = 0, words = 0, bytes = 0;
@@ -365,6 +377,6 @@ extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codeboo
     }
   std::memcpy(a.ksign, cbk->sign_bits, sizeof(a.ksign));
   std::memcpy(a.vsign, cbv->sign_bits, sizeof(a.vsign));
-  const hipError_t e = kvq::launch_attend(a, cbk->d, cbk->bits, static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq::launch_attend(a, cbk->d, cbk->bits, p.nqw, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }

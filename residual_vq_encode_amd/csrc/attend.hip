@@ -11,11 +11,14 @@
 // every value one lookup and one FMA, and the output is rotated back once per query.
 //
 // Work split (flash decoding): the cached positions [0, S_kv) are cut into chunks. One wave
-// handles one (query vector, chunk) pair with the lane layout of the codec (L lanes per
-// head vector, C coordinates per lane, 64 / L cached positions per iteration); each group
-// of L lanes keeps its own online-softmax state, the groups are merged at the end of the
-// chunk, and the chunk's (max, sum, accumulator) goes to the caller's workspace.
-// attend_combine merges the chunks of each query vector and rotates the result back.
+// handles up to 4 query vectors that read the same key/value head, over one chunk, with the
+// codec's lane layout (L lanes per head vector, C coordinates per lane, 64 / L cached
+// positions per iteration; C = 16 when a wave serves several queries); each key and value
+// is decoded once for all of them. Each group of L lanes keeps its own online-softmax state,
+// the groups are merged at the end of the chunk, and each query's (max, sum, accumulator)
+// for the chunk goes to the caller's workspace.
+// attend_combine merges the chunks of each query vector (one block per vector) and rotates
+// the result back.
 // Scores are kept in base-2 units (the query carries log2(e)), so the exponentials are
 // single v_exp_f32 instructions.
 #include <hip/hip_runtime.h>
@@ -28,14 +31,30 @@
 
 namespace kvq {
 
-constexpr int kAttendWavesPerEU = 3;
+// Waves per SIMD the partial kernel is compiled for: 3 (168 registers per lane), 2 when a
+// wave carries 4 queries (their rotated queries and accumulators alone take 128 registers).
+template <int NQW>
+constexpr int attend_waves_per_eu() {
+  return NQW == 4 ? 2 : 3;
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int BITS>
-__global__ __launch_bounds__(kBlockThreads, kAttendWavesPerEU) void attend_partial(const AttendArgs a) {
-  using G = Layout<D>;
-  using S = CodeShape<D, BITS>;
+// Coordinates per lane of the attention layout: 16 when a wave serves several queries
+// (their rotated queries and accumulators are 2 * NQW * C registers per lane), else 32.
+template <int D, int NQW>
+constexpr int attend_cm() {
+  return (NQW > 1 && D >= 32 && D <= 512) ? 16 : 32;
+}
+
+// One wave: NQW query vectors that read the same key/value head (consecutive query heads of
+// one group, or consecutive query positions), over one chunk of cached positions. Each key
+// and value is decoded once for all NQW queries.
+template <int D, int BITS, int NQW>
+__global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void attend_partial(const AttendArgs a) {
+  constexpr int CM = attend_cm<D, NQW>();
+  using G = Layout<D, CM>;
+  using S = CodeShape<D, BITS, CM>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH, NWL = S::NWL;
   constexpr int NZ = 1 << (2 * BITS);
 
@@ -59,25 +78,34 @@ __global__ __launch_bounds__(kBlockThreads, kAttendWavesPerEU) void attend_parti
   const int vl = lane >> LOG_L;
   uint32_t* cs = cstage[S::STAGED ? wv : 0];
 
-  // Unit u of this wave. Consecutive units share (b, hkv, chunk), so the waves of a block
-  // read the same packed keys and values.
-  const int64_t GQ = static_cast<int64_t>(a.group) * a.Sq;
+  // Unit u of this wave: (b, hkv, chunk, query group), the query group fastest, so the waves
+  // of a block read the same packed keys and values.
+  const int64_t GQ = static_cast<int64_t>(a.group) * a.Sq;  // query vectors per key/value head
+  const int64_t NG = GQ / NQW;
   const int64_t u = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wv;
-  if (u >= a.n_q * a.n_splits) return;  // wave-uniform; no barrier follows
-  const int64_t qi = u % GQ;
-  const int64_t r = u / GQ;
+  if (u >= (a.n_q / NQW) * a.n_splits) return;  // wave-uniform; no barrier follows
+  const int64_t qg = u % NG;
+  const int64_t r = u / NG;
   const int sp = static_cast<int>(r % a.n_splits);
   const int64_t bh = r / a.n_splits;  // b * Hkv + hkv
   const int64_t b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int64_t Hq = static_cast<int64_t>(a.Hkv) * a.group;
-  const int64_t qv = (b * Hq + hkv * a.group + qi / a.Sq) * a.Sq + qi % a.Sq;
+  int64_t qv[NQW];
+#pragma unroll
+  for (int k = 0; k < NQW; ++k) {
+    const int64_t qi = qg * NQW + k;
+    qv[k] = (b * Hq + hkv * a.group + qi / a.Sq) * a.Sq + qi % a.Sq;
+  }
 
-  // 1. This lane's slice of the rotated query, y = H diag(s_k) q (every group of L lanes
+  // 1. This lane's slices of the rotated queries, y = H diag(s_k) q (every group of L lanes
   //    holds a copy): stages 1-2 from v_dot2 on the fp16 pairs with the signs as weights,
   //    the rest in registers and across the group's lanes.
-  float qs[C];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qv * D + q * C);
+  float qs[NQW][C];
+  // (R q)_j = lane value * (-1)^popcount(q) / sqrt(D); scale and log2(e) ride along
+  const float qk = (__builtin_popcount(q) & 1) ? -a.qscale : a.qscale;
+#pragma unroll
+  for (int k = 0; k < NQW; ++k) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + qv[k] * D + q * C);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const uint4 v = qp[c];
@@ -88,19 +116,17 @@ __global__ __launch_bounds__(kBlockThreads, kAttendWavesPerEU) void attend_parti
         const uint32_t w1 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * g + 1];
         const float s0 = dot2_f16<0>(xh[2 * g], w0);
         const float d0 = dot2_f16<1>(xh[2 * g], w0);
-        float* o = qs + 8 * c + 4 * g;
+        float* o = qs[k] + 8 * c + 4 * g;
         o[0] = dot2_f16<0>(xh[2 * g + 1], w1, s0);
         o[1] = dot2_f16<1>(xh[2 * g + 1], w1, d0);
         o[2] = dot2_f16<2>(xh[2 * g + 1], w1, s0);
         o[3] = dot2_f16<3>(xh[2 * g + 1], w1, d0);
       }
     }
-    lane_stages<C, 4>(qs);
-    cross_stages<C, LOG_L>(qs, q);
-    // (R q)_j = lane value * (-1)^popcount(q) / sqrt(D); scale and log2(e) ride along
-    const float k = (__builtin_popcount(q) & 1) ? -a.qscale : a.qscale;
+    lane_stages<C, 4>(qs[k]);
+    cross_stages<C, LOG_L>(qs[k], q);
 #pragma unroll
-    for (int j = 0; j < C; ++j) qs[j] *= k;
+    for (int j = 0; j < C; ++j) qs[k][j] *= qk;
   }
 
   // 2. The chunk's cached positions, 64 / L per iteration (one per lane group), with the next
@@ -113,17 +139,22 @@ __global__ __launch_bounds__(kBlockThreads, kAttendWavesPerEU) void attend_parti
   auto fetch = [&](int64_t base) {
     const int64_t t = base + vl < t1 ? base + vl : t1 - 1;  // past the chunk: re-read its last key
     const int64_t row = rowbase + t;
-    load_lane_words<D, BITS>(a.k1, row, q, nk1);
-    load_lane_words<D, BITS>(a.k2, row, q, nk2);
-    load_lane_words<D, BITS>(a.v1, row, q, nv1);
-    load_lane_words<D, BITS>(a.v2, row, q, nv2);
+    load_lane_words<D, BITS, CM>(a.k1, row, q, nk1);
+    load_lane_words<D, BITS, CM>(a.k2, row, q, nk2);
+    load_lane_words<D, BITS, CM>(a.v1, row, q, nv1);
+    load_lane_words<D, BITS, CM>(a.v2, row, q, nv2);
     nkn = a.kn[row];
     nvn = a.vn[row];
   };
-  float m = -FLT_MAX, l = 0.f;  // running max (base 2) and sum of weights of this lane group
-  float acc[C];                 // running sum of weight * n_v * z_v, this lane's coordinates
+  float m[NQW], l[NQW];  // running max (base 2) and sum of weights of this lane group
+  float acc[NQW][C];     // running sum of weight * n_v * z_v, this lane's coordinates
 #pragma unroll
-  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+  for (int k = 0; k < NQW; ++k) {
+    m[k] = -FLT_MAX;
+    l[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc[k][j] = 0.f;
+  }
 
   fetch(t0);
   for (int64_t base = t0; base < t1; base += VW) {
@@ -134,155 +165,193 @@ __global__ __launch_bounds__(kBlockThreads, kAttendWavesPerEU) void attend_parti
     if (base + VW < t1) fetch(base + VW);
     const bool valid = base + vl < t1;
 
-    // score (base 2) = n_k * (scaled R q) . z_k, summed over the group's lanes
+    // scores (base 2) = n_k * (scaled R q) . z_k, summed over the group's lanes
     float z[C];
-    codes_to_z<D, BITS, true>(k1, k2, ztk, cs, lane, vl, q, z);
-    float d4[4] = {0.f, 0.f, 0.f, 0.f};
+    codes_to_z<D, BITS, true, CM>(k1, k2, ztk, cs, lane, vl, q, z);
+    float w[NQW];
 #pragma unroll
-    for (int j = 0; j < C; ++j) d4[j & 3] = __builtin_fmaf(qs[j], z[j], d4[j & 3]);
-    const float s = lane_sum<LOG_L>((d4[0] + d4[1]) + (d4[2] + d4[3])) * kn;
-
-    // online softmax; the rescale of the running state is skipped while the max holds
-    const float m_new = valid ? __builtin_fmaxf(m, s) : m;
-    const float w = valid ? exp2_fast(s - m_new) : 0.f;
-    if (m_new > m) {
-      const float f = exp2_fast(m - m_new);
-      l *= f;
+    for (int k = 0; k < NQW; ++k) {
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < C; ++j) acc[j] *= f;
-      m = m_new;
+      for (int j = 0; j < C; ++j) d4[j & 3] = __builtin_fmaf(qs[k][j], z[j], d4[j & 3]);
+      const float sc = lane_sum<LOG_L>((d4[0] + d4[1]) + (d4[2] + d4[3])) * kn;
+      // online softmax; the rescale of the running state is skipped while the max holds
+      const float m_new = valid ? __builtin_fmaxf(m[k], sc) : m[k];
+      w[k] = valid ? exp2_fast(sc - m_new) * vn : 0.f;
+      if (m_new > m[k]) {
+        const float f = exp2_fast(m[k] - m_new);
+        l[k] *= f;
+#pragma unroll
+        for (int j = 0; j < C; ++j) acc[k][j] *= f;
+        m[k] = m_new;
+      }
+      l[k] += valid ? exp2_fast(sc - m_new) : 0.f;
     }
-    l += w;
 
-    codes_to_z<D, BITS, true>(v1, v2, ztv, cs, lane, vl, q, z);
-    const float wn = w * vn;
+    codes_to_z<D, BITS, true, CM>(v1, v2, ztv, cs, lane, vl, q, z);
 #pragma unroll
-    for (int j = 0; j < C; ++j) acc[j] = __builtin_fmaf(wn, z[j], acc[j]);
+    for (int k = 0; k < NQW; ++k)
+#pragma unroll
+      for (int j = 0; j < C; ++j) acc[k][j] = __builtin_fmaf(w[k], z[j], acc[k][j]);
   }
 
-  // 3. Merge the lane groups (lanes with equal q), then group 0 writes the chunk's state.
+  // 3. Merge the lane groups (lanes with equal q), then group 0 writes each query's state.
 #pragma unroll
-  for (int off = L; off < 64; off <<= 1) {
-    const float mo = __shfl_xor(m, off), lo = __shfl_xor(l, off);
-    const float M = __builtin_fmaxf(m, mo);
-    const float f1 = exp2_fast(m - M), f2 = exp2_fast(mo - M);
-    l = l * f1 + lo * f2;
+  for (int k = 0; k < NQW; ++k) {
 #pragma unroll
-    for (int j = 0; j < C; ++j) acc[j] = acc[j] * f1 + __shfl_xor(acc[j], off) * f2;
-    m = M;
-  }
-  if (vl == 0) {
-    float* ws = a.ws + (qv * a.n_splits + sp) * (D + 4);
-    if (q == 0) {
-      ws[0] = m;
-      ws[1] = l;
+    for (int off = L; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(m[k], off), lo = __shfl_xor(l[k], off);
+      const float M = __builtin_fmaxf(m[k], mo);
+      const float f1 = exp2_fast(m[k] - M), f2 = exp2_fast(mo - M);
+      l[k] = l[k] * f1 + lo * f2;
+#pragma unroll
+      for (int j = 0; j < C; ++j) acc[k][j] = acc[k][j] * f1 + __shfl_xor(acc[k][j], off) * f2;
+      m[k] = M;
     }
-    float4* wa = reinterpret_cast<float4*>(ws + 4 + q * C);
+    if (vl == 0) {
+      float* ws = a.ws + (qv[k] * a.n_splits + sp) * (D + 4);
+      if (q == 0) {
+        ws[0] = m[k];
+        ws[1] = l[k];
+      }
+      float4* wa = reinterpret_cast<float4*>(ws + 4 + q * C);
 #pragma unroll
-    for (int c = 0; c < C / 4; ++c) wa[c] = make_float4(acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]);
+      for (int c = 0; c < C / 4; ++c)
+        wa[c] = make_float4(acc[k][4 * c], acc[k][4 * c + 1], acc[k][4 * c + 2], acc[k][4 * c + 3]);
+    }
   }
 }
 
+// One block per query vector. The block's threads form SG groups; group g merges chunks
+// g, g + SG, ... with each thread owning D / (1024 / SG) coordinates, the groups meet in LDS,
+// and the first wave rotates the merged vector back with the codec's lane layout.
+constexpr int kCombineThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(kBlockThreads) void attend_combine(const AttendArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void attend_combine(const AttendArgs a) {
   using G = Layout<D>;
-  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
+  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, CH = G::CH;
+  constexpr int SG = D >= kCombineThreads ? 1 : kCombineThreads / D;  // split groups
+  constexpr int TPG = kCombineThreads / SG;                            // threads per group
+  constexpr int CPT = D / TPG;                                     // coordinates per thread
 
   __shared__ uint32_t vx[D / 2];  // value signs as fp16 sign-bit masks
-  for (int m = threadIdx.x; m < D / 2; m += kBlockThreads) {
+  __shared__ float gm[SG], gs[SG];
+  __shared__ float ga[SG][D];
+  for (int m = threadIdx.x; m < D / 2; m += kCombineThreads) {
     const uint32_t s0 = (a.vsign[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
     const uint32_t s1 = (a.vsign[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
     vx[m] = (s0 ? 0x8000u : 0u) | (s1 ? 0x80000000u : 0u);
   }
-  __syncthreads();
+  const int64_t qv = blockIdx.x;
+  const int g = threadIdx.x / TPG, t = threadIdx.x % TPG;
 
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q = lane & (L - 1);
-  const int vl = lane >> LOG_L;
-  const int64_t qv0 = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wv) * VW;
-  if (qv0 >= a.n_q) return;  // wave-uniform
-  const int64_t qv = qv0 + vl;
-  const int64_t qc = qv < a.n_q ? qv : a.n_q - 1;  // lanes past the end work on a valid vector
-
-  // merge the chunks: M = max, sum = sum l e^(m - M), A = sum acc e^(m - M) (base 2)
-  float M = -FLT_MAX, sum = 0.f, A[C];
+  // merge this group's chunks: M = max, sum = sum l 2^(m - M), A = sum acc 2^(m - M)
+  float M = -FLT_MAX, sum = 0.f, A[CPT];
 #pragma unroll
-  for (int j = 0; j < C; ++j) A[j] = 0.f;
-  for (int sp = 0; sp < a.n_splits; ++sp) {
-    const float* ws = a.ws + (qc * a.n_splits + sp) * (D + 4);
+  for (int i = 0; i < CPT; ++i) A[i] = 0.f;
+#pragma unroll 4
+  for (int sp = g; sp < a.n_splits; sp += SG) {
+    const float* ws = a.ws + (qv * a.n_splits + sp) * (D + 4);
     const float ms = ws[0], ls = ws[1];
     const float Mn = __builtin_fmaxf(M, ms);
     const float f1 = exp2_fast(M - Mn), f2 = exp2_fast(ms - Mn);
     sum = sum * f1 + ls * f2;
-    const float4* wa = reinterpret_cast<const float4*>(ws + 4 + q * C);
 #pragma unroll
-    for (int c = 0; c < C / 4; ++c) {
-      const float4 v = wa[c];
-      A[4 * c] = A[4 * c] * f1 + v.x * f2;
-      A[4 * c + 1] = A[4 * c + 1] * f1 + v.y * f2;
-      A[4 * c + 2] = A[4 * c + 2] * f1 + v.z * f2;
-      A[4 * c + 3] = A[4 * c + 3] * f1 + v.w * f2;
-    }
+    for (int i = 0; i < CPT; ++i) A[i] = A[i] * f1 + ws[4 + t * CPT + i] * f2;
     M = Mn;
   }
-
-  // out = diag(s_v) H (A / sum) / sqrt(D), rounded to fp16
-  float K = a.inv_sqrt_d / sum;
-  if (__builtin_popcount(q) & 1) K = -K;
-  uint32_t o[C / 2];
-  unrotate_f16<D>(A, K, q, o);
-  if (qv < a.n_q) {
-    uint4* dst = reinterpret_cast<uint4*>(a.out + qv * D + q * C);
+  if (t == 0) {
+    gm[g] = M;
+    gs[g] = sum;
+  }
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int p = q * (C / 2) + 4 * c;
-      dst[c] = make_uint4(o[4 * c] ^ vx[p], o[4 * c + 1] ^ vx[p + 1], o[4 * c + 2] ^ vx[p + 2], o[4 * c + 3] ^ vx[p + 3]);
+  for (int i = 0; i < CPT; ++i) ga[g][t * CPT + i] = A[i];
+  __syncthreads();
+
+  // first wave: lanes q < L of lane group 0 own coordinates [C q, C q + C)
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int q = lane & (L - 1);
+    const int vl = lane >> LOG_L;
+    float Mt = -FLT_MAX;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) Mt = __builtin_fmaxf(Mt, gm[k]);
+    float St = 0.f, z[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) z[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) {
+      const float f = exp2_fast(gm[k] - Mt);
+      St += gs[k] * f;
+#pragma unroll
+      for (int j = 0; j < C; ++j) z[j] += ga[k][q * C + j] * f;
+    }
+    // out = diag(s_v) H (A / sum) / sqrt(D), rounded to fp16
+    float K = a.inv_sqrt_d / St;
+    if (__builtin_popcount(q) & 1) K = -K;
+    uint32_t o[C / 2];
+    unrotate_f16<D>(z, K, q, o);
+    if (vl == 0) {
+      uint4* dst = reinterpret_cast<uint4*>(a.out + qv * D + q * C);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int p = q * (C / 2) + 4 * c;
+        dst[c] = make_uint4(o[4 * c] ^ vx[p], o[4 * c + 1] ^ vx[p + 1], o[4 * c + 2] ^ vx[p + 2], o[4 * c + 3] ^ vx[p + 3]);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------------------ dispatch
 
-template <int D, int BITS>
+template <int D, int BITS, int NQW>
 static hipError_t launch_attend_t(const AttendArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<AttendArgs*>(&a)};
-  const int64_t units = a.n_q * a.n_splits;
+  const int64_t units = (a.n_q / NQW) * a.n_splits;
   const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > INT_MAX) return hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attend_partial<D, BITS>), dim3(static_cast<int>(blocks)),
-                                 dim3(kBlockThreads), args, 0, stream);
+  if (blocks > INT_MAX || a.n_q > INT_MAX) return hipErrorInvalidValue;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attend_partial<D, BITS, NQW>),
+                                 dim3(static_cast<int>(blocks)), dim3(kBlockThreads), args, 0, stream);
   if (e != hipSuccess) return e;
-  const int64_t waves = (a.n_q + Layout<D>::VW - 1) / Layout<D>::VW;
-  const int64_t cblocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (cblocks > INT_MAX) return hipErrorInvalidValue;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_combine<D>), dim3(static_cast<int>(cblocks)),
-                         dim3(kBlockThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_combine<D>), dim3(static_cast<int>(a.n_q)),
+                         dim3(kCombineThreads), args, 0, stream);
+}
+
+template <int D, int BITS>
+static auto attend_nqw(int nqw) -> hipError_t (*)(const AttendArgs&, hipStream_t) {
+  if (nqw == 1) return launch_attend_t<D, BITS, 1>;
+  if constexpr (D <= 512) {
+    if (nqw == 2) return launch_attend_t<D, BITS, 2>;
+    if (nqw == 4) return launch_attend_t<D, BITS, 4>;
+  }
+  return nullptr;
 }
 
 template <int D>
-static auto attend_fn(int bits) -> hipError_t (*)(const AttendArgs&, hipStream_t) {
+static auto attend_fn(int bits, int nqw) -> hipError_t (*)(const AttendArgs&, hipStream_t) {
   switch (bits) {
-    case 1: return launch_attend_t<D, 1>;
-    case 2: return launch_attend_t<D, 2>;
-    case 3: return launch_attend_t<D, 3>;
-    case 4: return launch_attend_t<D, 4>;
+    case 1: return attend_nqw<D, 1>(nqw);
+    case 2: return attend_nqw<D, 2>(nqw);
+    case 3: return attend_nqw<D, 3>(nqw);
+    case 4: return attend_nqw<D, 4>(nqw);
     default: return nullptr;
   }
 }
 
 // Launcher used by api.cpp: both kernels on `stream`, the combine after the partials.
-hipError_t launch_attend(const AttendArgs& a, int d, int bits, hipStream_t stream) {
+// nqw: query vectors per wave (1, 2 or 4; a divisor of group * Sq; 1 for d = 1024).
+hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream) {
   hipError_t (*f)(const AttendArgs&, hipStream_t) = nullptr;
   switch (d) {
-    case 8: f = attend_fn<8>(bits); break;
-    case 16: f = attend_fn<16>(bits); break;
-    case 32: f = attend_fn<32>(bits); break;
-    case 64: f = attend_fn<64>(bits); break;
-    case 128: f = attend_fn<128>(bits); break;
-    case 256: f = attend_fn<256>(bits); break;
-    case 512: f = attend_fn<512>(bits); break;
-    case 1024: f = attend_fn<1024>(bits); break;
+    case 8: f = attend_fn<8>(bits, nqw); break;
+    case 16: f = attend_fn<16>(bits, nqw); break;
+    case 32: f = attend_fn<32>(bits, nqw); break;
+    case 64: f = attend_fn<64>(bits, nqw); break;
+    case 128: f = attend_fn<128>(bits, nqw); break;
+    case 256: f = attend_fn<256>(bits, nqw); break;
+    case 512: f = attend_fn<512>(bits, nqw); break;
+    case 1024: f = attend_fn<1024>(bits, nqw); break;
     default: break;
   }
   return f ? f(a, stream) : hipErrorInvalidValue;

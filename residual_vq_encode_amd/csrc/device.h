@@ -17,15 +17,18 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// How one vector of D coordinates maps onto lanes.
-template <int D>
+// How one vector of D coordinates maps onto lanes: C = min(D, CM) consecutive coordinates
+// per lane (CM = 32 for the codec kernels; the attention kernels use 16 to leave registers
+// for several queries).
+template <int D, int CM = 32>
 struct Layout {
-  static constexpr int C = D < 32 ? D : 32;       // coordinates per lane
+  static constexpr int C = D < CM ? D : CM;       // coordinates per lane
   static constexpr int L = D / C;                 // lanes per vector
   static constexpr int LOG_L = __builtin_ctz(L);  // butterfly stages across lanes
   static constexpr int VW = 64 / L;               // vectors per wave tile
   static constexpr int CH = C / 8;                // 16-byte input chunks per lane
   static_assert(D >= 8 && D <= 1024 && (D & (D - 1)) == 0, "D must be a power of two in [8, 1024]");
+  static_assert(CM >= 8 && L <= 32, "at least 8 coordinates per lane, at most 32 lanes per vector");
 };
 
 
@@ -311,29 +314,33 @@ __device__ __forceinline__ uint32_t unpack4x3(uint32_t v) {  // 12 bits -> 4 byt
 // ------------------------------------------------------------------------------ code access
 
 // Where a lane finds the codes of its C coordinates in a packed stream.
-template <int D, int BITS>
+template <int D, int BITS, int CM = 32>
 struct CodeShape {
-  static constexpr int C = Layout<D>::C, L = Layout<D>::L;
+  static constexpr int C = Layout<D, CM>::C, L = Layout<D, CM>::L;
   static constexpr int EPW = 32 / BITS;                // codes per word
   static constexpr int NW = (D + EPW - 1) / EPW;       // words per vector per stream
   static constexpr bool STAGED = BITS == 3 && L > 1;   // 10-code words straddle lanes
+  static constexpr bool SUB = !STAGED && L > 1 && C < EPW;  // a word holds several lanes' codes
   // words a lane loads per stream: its own NWL consecutive words, or for STAGED words
-  // q, q + L, ... of the vector (regrouped through LDS by stage_codes)
-  static constexpr int NWL = STAGED ? (NW + L - 1) / L : (L == 1 ? NW : C / EPW);
+  // q, q + L, ... of the vector (regrouped through LDS by stage_codes), or for SUB the one
+  // word holding its codes, shifted so that they start at bit 0
+  static constexpr int NWL = STAGED ? (NW + L - 1) / L : SUB ? 1 : (L == 1 ? NW : C / EPW);
   static constexpr int CSTREAM = 64 * C / 4;           // STAGED: LDS dwords per stream per wave
 };
 
 // Loads the words of one stream that lane q of the vector in cache row `row` needs.
-template <int D, int BITS>
+template <int D, int BITS, int CM = 32>
 __device__ __forceinline__ void load_lane_words(const uint32_t* p, int64_t row, int q,
-                                                uint32_t (&w)[CodeShape<D, BITS>::NWL]) {
-  using S = CodeShape<D, BITS>;
+                                                uint32_t (&w)[CodeShape<D, BITS, CM>::NWL]) {
+  using S = CodeShape<D, BITS, CM>;
   if constexpr (S::STAGED) {
 #pragma unroll
     for (int k = 0; k < S::NWL; ++k) {
       const int wi = q + S::L * k < S::NW ? q + S::L * k : S::NW - 1;
       w[k] = p[row * S::NW + wi];
     }
+  } else if constexpr (S::SUB) {
+    w[0] = p[row * S::NW + (q * S::C) / S::EPW] >> (BITS * ((q * S::C) % S::EPW));
   } else {
     load_words<S::NWL>(p + row * S::NW + q * S::NWL, w);
   }
@@ -342,10 +349,10 @@ __device__ __forceinline__ void load_lane_words(const uint32_t* p, int64_t row, 
 // STAGED only: lane q of vector vl unpacks its words q, q + L, ... into one byte per code at
 // bytes [D vl, D vl + D) of the wave's LDS stream `cs` (every lane of the vector writes a
 // disjoint part; the caller orders these writes before the reads of codes_of).
-template <int D, int BITS>
-__device__ __forceinline__ void stage_codes(const uint32_t (&w)[CodeShape<D, BITS>::NWL], uint32_t* cs, int vl,
+template <int D, int BITS, int CM = 32>
+__device__ __forceinline__ void stage_codes(const uint32_t (&w)[CodeShape<D, BITS, CM>::NWL], uint32_t* cs, int vl,
                                             int q) {
-  using S = CodeShape<D, BITS>;
+  using S = CodeShape<D, BITS, CM>;
 #pragma unroll
   for (int k = 0; k < S::NWL; ++k) {
     const int wi = q + S::L * k;
@@ -365,32 +372,32 @@ __device__ __forceinline__ void stage_codes(const uint32_t (&w)[CodeShape<D, BIT
 }
 
 // Code of local coordinate j (0 <= j < C) of this lane, from its own words (not STAGED).
-template <int D, int BITS>
-__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[CodeShape<D, BITS>::NWL], int j) {
-  using S = CodeShape<D, BITS>;
+template <int D, int BITS, int CM = 32>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[CodeShape<D, BITS, CM>::NWL], int j) {
+  using S = CodeShape<D, BITS, CM>;
   return (w[j / S::EPW] >> (BITS * (j % S::EPW))) & ((1u << BITS) - 1u);
 }
 
 // Dequantized rotated-domain coordinates z[j] = table[(i1 << BITS) | i2] of this lane
 // (i2 = 0 when TWO is false). `zt` is the LDS table, `cs` the wave's LDS staging area for
 // STAGED codes (two streams of CSTREAM dwords; unused otherwise).
-template <int D, int BITS, bool TWO>
-__device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BITS>::NWL],
-                                           const uint32_t (&w2)[CodeShape<D, BITS>::NWL], const float* zt,
-                                           uint32_t* cs, int lane, int vl, int q, float (&z)[Layout<D>::C]) {
-  using S = CodeShape<D, BITS>;
+template <int D, int BITS, bool TWO, int CM = 32>
+__device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BITS, CM>::NWL],
+                                           const uint32_t (&w2)[CodeShape<D, BITS, CM>::NWL], const float* zt,
+                                           uint32_t* cs, int lane, int vl, int q, float (&z)[Layout<D, CM>::C]) {
+  using S = CodeShape<D, BITS, CM>;
   constexpr int C = S::C;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   if constexpr (!S::STAGED) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-      const uint32_t i1 = code_at<D, BITS>(w1, j);
-      const uint32_t i2 = TWO ? code_at<D, BITS>(w2, j) : 0u;
+      const uint32_t i1 = code_at<D, BITS, CM>(w1, j);
+      const uint32_t i2 = TWO ? code_at<D, BITS, CM>(w2, j) : 0u;
       z[j] = zt[(i1 << BITS) | i2];
     }
   } else {
-    stage_codes<D, BITS>(w1, cs, vl, q);
-    if constexpr (TWO) stage_codes<D, BITS>(w2, cs + S::CSTREAM, vl, q);
+    stage_codes<D, BITS, CM>(w1, cs, vl, q);
+    if constexpr (TWO) stage_codes<D, BITS, CM>(w2, cs + S::CSTREAM, vl, q);
     wave_lds_fence();
 #pragma unroll
     for (int d4 = 0; d4 < C / 4; ++d4) {
@@ -410,12 +417,12 @@ __device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BIT
 // o = RN16(K * (H z)) per coordinate pair, H applied in registers then across the L lanes
 // of the vector. K must carry the lane's sign (-1)^popcount(q) (see cross_stage); the
 // caller applies the final diag(s) to the fp16 pairs (an XOR of sign bits).
-template <int D>
-__device__ __forceinline__ void unrotate_f16(float (&z)[Layout<D>::C], float K, int q,
-                                             uint32_t (&o)[Layout<D>::C / 2]) {
-  constexpr int C = Layout<D>::C;
+template <int D, int CM = 32>
+__device__ __forceinline__ void unrotate_f16(float (&z)[(Layout<D, CM>::C)], float K, int q,
+                                             uint32_t (&o)[(Layout<D, CM>::C) / 2]) {
+  constexpr int C = Layout<D, CM>::C;
   lane_stages<C, 1>(z);
-  cross_stages<C, Layout<D>::LOG_L>(z, q);
+  cross_stages<C, Layout<D, CM>::LOG_L>(z, q);
 #pragma unroll
   for (int m = 0; m < C / 2; ++m) {
     const half2_t h = {static_cast<_Float16>(z[2 * m] * K), static_cast<_Float16>(z[2 * m + 1] * K)};

@@ -68,6 +68,17 @@ def test_attend_grid(d, bits):
     _check(d, bits, B=2, Hq=4, Hkv=2, Sq=2, S_cap=45, S_kv=37, seed=d + bits)
 
 
+# (Hq, Hkv, Sq): query vectors per key/value head 1, 2, 4 (all from Sq) and 6 (2 heads x 3
+# positions), so that waves carry 1, 2, 4 and 2 queries and the query-to-head map is mixed.
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("bits", [1, 3])
+@pytest.mark.parametrize("shape", [(3, 3, 1), (6, 3, 1), (2, 2, 4), (4, 2, 3)])
+def test_attend_queries_per_wave(d, bits, shape):
+    Hq, Hkv, Sq = shape
+    _say(f"attend d={d} bits={bits} Hq={Hq} Hkv={Hkv} Sq={Sq}")
+    _check(d, bits, B=2, Hq=Hq, Hkv=Hkv, Sq=Sq, S_cap=70, S_kv=61, seed=3 * d + bits + Hq)
+
+
 @pytest.mark.parametrize("S_kv", [1, 2, 15, 16, 17, 127, 128, 129, 1000, 4097])
 def test_attend_lengths(S_kv):
     _say(f"attend S_kv={S_kv}")

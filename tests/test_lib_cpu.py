@@ -174,21 +174,30 @@ def test_attend_host_side_argument_checks():
     assert att(ptrs=(A, A, None, A, A, A)) == -1
     assert att(q=A + 2) == -3 and att(out=A + 8) == -3 and att(ws=A + 4) == -3
     assert att(ptrs=(A + 4, A, A, A, A, A)) == -3 and att(ptrs=(A, A, A + 2, A, A, A)) == -3
-    need = kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 50)
+    need = kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 50)
     assert need > 0 and att(wsb=need - 1) == -4
-    assert lib.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 50, None) == -1
+    assert lib.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 50, None) == -1
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_rvq_attend_workspace_size(96, 1, 4, 1, 50)
+        kvq.kvq_rvq_attend_workspace_size(96, 1, 4, 1, 2, 50)
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 0)
-    # plan: chunks of whole 16-position iterations, about 8192 wave units, at least 8 iterations each
-    for (B, Hq, Sq, S_kv) in ((1, 32, 1, 32768), (1, 1, 1, 5), (4, 8, 3, 1000), (1, 32, 1, 1)):
+        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 3, 50)
+    # plan: nqw query vectors per wave (4, 2 or 1, dividing the query vectors per key/value
+    # head); chunks of whole wave iterations (64 / (d / 16) positions with nqw > 1, else
+    # 64 / (d / 32)), about 2048 waves, at least 8 iterations each
+    for (d, B, Hq, Sq, Hkv, S_kv, nqw) in ((128, 1, 32, 1, 8, 32768, 4), (128, 1, 1, 1, 1, 5, 1),
+                                           (128, 4, 8, 3, 4, 1000, 2), (128, 1, 32, 1, 32, 1, 1),
+                                           (64, 2, 6, 1, 2, 700, 1), (1024, 1, 8, 1, 2, 3000, 1),
+                                           (16, 1, 4, 2, 1, 77, 4)):
         nq = B * Hq * Sq
-        splits0 = -(-8192 // nq)
+        cm = 16 if nqw > 1 and d >= 32 else 32
+        vw = 64 // (d // min(d, cm))
+        splits0 = -(-2048 * nqw // nq)
         chunk = -(-S_kv // splits0)
-        chunk = max(-(-chunk // 16) * 16, 128)
+        chunk = max(-(-chunk // vw) * vw, 8 * vw)
         n_splits = -(-S_kv // chunk)
-        assert kvq.kvq_rvq_attend_workspace_size(128, B, Hq, Sq, S_kv) == nq * n_splits * (128 + 4) * 4
+        assert kvq.kvq_rvq_attend_workspace_size(d, B, Hq, Sq, Hkv, S_kv) == nq * n_splits * (d + 4) * 4
 
 
 def test_python_binding_rejects_cpu_tensors():
