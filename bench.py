@@ -56,7 +56,7 @@ ATTEND_WORKLOADS = {"attend_decode": {"B": 1, "Hq": 32, "Hkv": 8, "Sq": 1, "S_kv
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kernels.hip", "params.h"):
+    for f in ("kernels.hip", "device.h", "params.h"):
         h.update(open(os.path.join(ROOT, "residual_vq_encode_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -344,6 +344,8 @@ def bench_attend(args) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     us = e0.elapsed_time(e1) * 1e3 / K
+    gq = (Hq // Hkv) * Sq  # query vectors per key/value head; a wave serves nqw of them
+    nqw = 4 if gq % 4 == 0 and D <= 512 else 2 if gq % 2 == 0 and D <= 512 else 1
     cache_bytes = B * Hkv * S * 2 * (2 * nw * 4 + 4)
     alg = cache_bytes + 2 * B * Hq * Sq * D * 2
     gbps = alg / (us * 1e-6) / 1e9
@@ -384,7 +386,7 @@ def bench_attend(args) -> int:
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": alg,
-                     "kernel": f"kvq::attend_partial<{D}, {bits}> + attend_combine<{D}>"},
+                     "kernel": f"kvq::attend_partial<{D}, {bits}, {nqw}> + attend_combine<{D}>"},
         "cpu_baseline": {"value": round(alg / dt_oracle / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
                          "sample": f"the whole step ({B * Hq * Sq} query vectors over {S} positions), "
                                    f"{dt_oracle:.1f} s wall, numpy float64 oracle"},

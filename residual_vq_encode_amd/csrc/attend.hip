@@ -40,6 +40,64 @@ constexpr int attend_waves_per_eu() {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Softmax reference slack (base-2 units): a lane group's exponentials are taken against a
+// reference that is moved only when a score exceeds it by more than this, so the running
+// state is rescaled a few times per chunk instead of at every new maximum; the weights stay
+// below 2^8 and the sums lose nothing (their relative precision is what matters).
+constexpr float kRefSlack = 8.f;
+
+// b = 1, 2 or 4: the codes of P = 4 / b consecutive coordinates fill one nibble of a packed
+// word. One byte made of a nibble of each stream (stage 1 low, stage 2 high) indexes a table
+// of the P dequantized values c1[i1] + c2[i2], so a lane reads P coordinates with one LDS
+// load and one shift.
+template <int BITS>
+constexpr int nibble_coords() {
+  return BITS == 3 ? 0 : 4 / BITS;
+}
+
+// The table: entry e holds, for p < P, c1[i1] + c2[i2] with i1 = code p of nibble e & 15 and
+// i2 = code p of nibble e >> 4, taken from zt[(i1 << BITS) | i2].
+template <int BITS>
+__device__ __forceinline__ void fill_nibble_table(const float* zt, float* tab) {
+  constexpr int P = nibble_coords<BITS>();
+  constexpr uint32_t M = (1u << BITS) - 1u;
+  for (int e = threadIdx.x; e < 256; e += kBlockThreads)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t i1 = (e >> (BITS * p)) & M, i2 = ((e >> 4) >> (BITS * p)) & M;
+      tab[e * P + p] = zt[(i1 << BITS) | i2];
+    }
+}
+
+// z[j] (j < C) of this lane from its words of both streams (codes of coordinate j at bits
+// [BITS j, BITS j + BITS) of the lane's word sequence).
+template <int BITS, int C, int NWL>
+__device__ __forceinline__ void nibble_z(const uint32_t (&w1)[NWL], const uint32_t (&w2)[NWL], const float* tab,
+                                         float (&z)[C]) {
+  constexpr int P = nibble_coords<BITS>();
+  constexpr int NIB = C / P;  // nibbles per stream that hold this lane's codes
+#pragma unroll
+  for (int w = 0; w < (NIB + 7) / 8; ++w) {
+    // byte k of lo: nibbles 2k of both words; of hi: nibbles 2k + 1
+    const uint32_t lo = (w1[w] & 0x0F0F0F0Fu) | ((w2[w] << 4) & 0xF0F0F0F0u);
+    const uint32_t hi = ((w1[w] >> 4) & 0x0F0F0F0Fu) | (w2[w] & 0xF0F0F0F0u);
+#pragma unroll
+    for (int t = 0; t < 8 && 8 * w + t < NIB; ++t) {
+      const uint32_t e = ((t & 1 ? hi : lo) >> (8 * (t >> 1))) & 0xFFu;
+      const int j0 = P * (8 * w + t);
+      if constexpr (P == 4) {
+        const float4 v = reinterpret_cast<const float4*>(tab)[e];
+        z[j0] = v.x; z[j0 + 1] = v.y; z[j0 + 2] = v.z; z[j0 + 3] = v.w;
+      } else if constexpr (P == 2) {
+        const float2 v = reinterpret_cast<const float2*>(tab)[e];
+        z[j0] = v.x; z[j0 + 1] = v.y;
+      } else {
+        z[j0] = tab[e];
+      }
+    }
+  }
+}
+
 // Coordinates per lane of the attention layout: 16 when a wave serves several queries
 // (their rotated queries and accumulators are 2 * NQW * C registers per lane), else 32.
 template <int D, int NQW>
@@ -57,13 +115,22 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   using S = CodeShape<D, BITS, CM>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH, NWL = S::NWL;
   constexpr int NZ = 1 << (2 * BITS);
+  constexpr int P = nibble_coords<BITS>();
+  constexpr int NT = P ? 256 * P : NZ;  // floats per LDS table
 
-  __shared__ float ztk[NZ], ztv[NZ];
+  // z tables: by nibble pair (b = 1, 2, 4) or by (i1 << b) | i2 (b = 3)
+  __shared__ __align__(16) float ztk[NT];
+  __shared__ __align__(16) float ztv[NT];
   __shared__ uint32_t kx[D / 2];  // key signs as fp16 sign-bit masks, one word per coordinate pair
   __shared__ uint32_t cstage[S::STAGED ? kWavesPerBlock : 1][S::STAGED ? 2 * S::CSTREAM : 1];
-  for (int i = threadIdx.x; i < NZ; i += kBlockThreads) {
-    ztk[i] = a.ztab_k[i];
-    ztv[i] = a.ztab_v[i];
+  if constexpr (P != 0) {
+    fill_nibble_table<BITS>(a.ztab_k, ztk);
+    fill_nibble_table<BITS>(a.ztab_v, ztv);
+  } else {
+    for (int i = threadIdx.x; i < NZ; i += kBlockThreads) {
+      ztk[i] = a.ztab_k[i];
+      ztv[i] = a.ztab_v[i];
+    }
   }
   for (int m = threadIdx.x; m < D / 2; m += kBlockThreads) {
     const uint32_t s0 = (a.ksign[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
@@ -146,7 +213,7 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
     nkn = a.kn[row];
     nvn = a.vn[row];
   };
-  float m[NQW], l[NQW];  // running max (base 2) and sum of weights of this lane group
+  float m[NQW], l[NQW];  // softmax reference (base 2) and sum of weights of this lane group
   float acc[NQW][C];     // running sum of weight * n_v * z_v, this lane's coordinates
 #pragma unroll
   for (int k = 0; k < NQW; ++k) {
@@ -167,28 +234,31 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
 
     // scores (base 2) = n_k * (scaled R q) . z_k, summed over the group's lanes
     float z[C];
-    codes_to_z<D, BITS, true, CM>(k1, k2, ztk, cs, lane, vl, q, z);
+    if constexpr (P != 0) nibble_z<BITS>(k1, k2, ztk, z);
+    else codes_to_z<D, BITS, true, CM>(k1, k2, ztk, cs, lane, vl, q, z);
     float w[NQW];
 #pragma unroll
     for (int k = 0; k < NQW; ++k) {
       float d4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < C; ++j) d4[j & 3] = __builtin_fmaf(qs[k][j], z[j], d4[j & 3]);
-      const float sc = lane_sum<LOG_L>((d4[0] + d4[1]) + (d4[2] + d4[3])) * kn;
-      // online softmax; the rescale of the running state is skipped while the max holds
-      const float m_new = valid ? __builtin_fmaxf(m[k], sc) : m[k];
-      w[k] = valid ? exp2_fast(sc - m_new) * vn : 0.f;
-      if (m_new > m[k]) {
-        const float f = exp2_fast(m[k] - m_new);
+      const float dot = lane_sum<LOG_L>((d4[0] + d4[1]) + (d4[2] + d4[3]));  // every lane takes part
+      const float sc = valid ? dot * kn : -FLT_MAX;
+      // online softmax against the reference m (see kRefSlack)
+      if (sc > m[k] + kRefSlack) {
+        const float f = exp2_fast(m[k] - sc);
         l[k] *= f;
 #pragma unroll
         for (int j = 0; j < C; ++j) acc[k][j] *= f;
-        m[k] = m_new;
+        m[k] = sc;
       }
-      l[k] += valid ? exp2_fast(sc - m_new) : 0.f;
+      const float e = valid ? exp2_fast(sc - m[k]) : 0.f;
+      l[k] += e;
+      w[k] = e * vn;
     }
 
-    codes_to_z<D, BITS, true, CM>(v1, v2, ztv, cs, lane, vl, q, z);
+    if constexpr (P != 0) nibble_z<BITS>(v1, v2, ztv, z);
+    else codes_to_z<D, BITS, true, CM>(v1, v2, ztv, cs, lane, vl, q, z);
 #pragma unroll
     for (int k = 0; k < NQW; ++k)
 #pragma unroll
