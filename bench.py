@@ -48,6 +48,10 @@ WORKLOADS = {
     # the single-stage codec (stage 1 only, one code stream) on the Llama layer
     "llama_layer_mse": ("llama_layer", 2, 8, 1),
 }
+# 1-bit sign codes of the Llama layer's keys: the RaBitQ-style code of the rotated vector
+# (D bits + fp32 norm per vector) and the QJL sketch with m = 128 rows (128 bits + fp16 norm)
+SIGN_WORKLOADS = {"rabitq_llama_layer": ("llama_layer", "rabitq", 0, 8),
+                  "qjl_llama_layer_m128": ("llama_layer", "qjl", 128, 8)}
 # attention over packed caches: one decode step of a GQA layer (32 query heads over 8
 # key/value heads of the gqa_long cache shape [1, 8, 32768, 128], b = 2, keys and values)
 ATTEND_WORKLOADS = {"attend_decode": {"B": 1, "Hq": 32, "Hkv": 8, "Sq": 1, "S_kv": 32768, "D": 128, "bits": 2,
@@ -137,7 +141,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama_layer", choices=sorted(WORKLOADS) + sorted(ATTEND_WORKLOADS))
+    ap.add_argument("--workload", default="llama_layer",
+                    choices=sorted(WORKLOADS) + sorted(ATTEND_WORKLOADS) + sorted(SIGN_WORKLOADS))
     ap.add_argument("--pool", type=int, default=None, help="distinct input tensors to rotate through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,6 +175,8 @@ def main() -> int:
         return 2
     if args.workload in ATTEND_WORKLOADS:
         return bench_attend(args)
+    if args.workload in SIGN_WORKLOADS:
+        return bench_signcodes(args)
     wname, bits, pool_default, stages = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wname]
     spec = w.tensors[0]
@@ -292,6 +299,118 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(spec, signs, bits, stages)
     print(json.dumps(result), flush=True)
     return 0 if parity_ok else 1
+
+
+def bench_signcodes(args) -> int:
+    """One 1-bit sign-code encoder over the workload tensor: K launches back to back over a
+    pool of distinct inputs and outputs, events around the group, then a parity re-check of
+    the last output on a sample of its vectors."""
+    import numpy as np
+    import torch
+
+    import residual_vq_encode_amd as kvq
+    import synth
+    from oracle import packing, signcodes
+
+    wname, kind, m, pool_default = SIGN_WORKLOADS[args.workload]
+    w = synth.WORKLOADS[wname]
+    spec = w.tensors[0]
+    P = args.pool or pool_default
+    dev = torch.device("cuda:0")
+    B, H, S, D = spec.B, spec.H, spec.S, spec.D
+    n_vec = B * H * S
+    xs = [synth.tensor(spec, device=dev)]
+    for i in range(1, P):
+        xs.append(synth.tensor(synth.TensorSpec(B, H, S, D, spec.kind, spec.seed + 1000 * i), device=dev))
+    stream = torch.cuda.current_stream()
+    if kind == "rabitq":
+        signs = synth.signs(w.sign_seed, D).numpy()
+        cb = kvq.build_codebooks(D, 1, signs)
+        nw = cb.n_words
+        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(P)]
+        ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(P)]
+
+        def enc(j):
+            kvq.kvq_rabitq_encode_pack(cb, xs[j], ps[j], ns[j], 0, stream)
+        out_bytes, norm_bytes, kname = nw * 4, 4, f"kvq::encode_kernel<{D}, 1, true, 0>"
+    else:
+        sk = synth.tensor(synth.TensorSpec(1, 1, m, D, "gauss", 707), device=dev).reshape(m, D).contiguous()
+        nw = m // 32
+        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(P)]
+        ns = [torch.empty((B, H, S), dtype=torch.float16, device=dev) for _ in range(P)]
+
+        def enc(j):
+            kvq.kvq_qjl_encode_pack(sk, xs[j], ps[j], ns[j], 0, stream)
+        out_bytes, norm_bytes, kname = nw * 4, 2, f"kvq::qjl_encode_kernel<{D}, {m // 32}, true>"
+
+    for i in range(args.warmup):
+        enc(i % P)
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        enc((args.warmup + i) % P)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    us = e0.elapsed_time(e1) * 1e3 / K
+    alg = n_vec * (D * 2 + out_bytes)
+    gbps = alg / (us * 1e-6) / 1e9
+
+    # parity re-check on a strided sample of the last timed output, and the oracle's time
+    j = (args.warmup + K - 1) % P
+    idx = torch.arange(0, n_vec, max(1, n_vec // 65536))
+    rows = xs[j].reshape(-1, D)[idx.to(dev)].cpu().numpy()
+    dev_p = ps[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
+    dev_n = ns[j].reshape(-1)[idx.to(dev)].cpu().numpy()
+    t0 = time.perf_counter()
+    if kind == "rabitq":
+        ref = signcodes.rabitq_encode(rows, signs)
+        diff = packing.unpack(dev_p, 1, D) != ref["bits"]
+        in_window = bool(np.all(np.abs(ref["y"][diff]) <= 1e-5 / math.sqrt(D)))
+        norm_ok = bool(np.all(np.abs(dev_n - ref["norm64"]) <= 1e-6 * ref["norm64"]))
+    else:
+        ref = signcodes.qjl_encode(rows, sk.cpu().numpy())
+        diff = packing.unpack(dev_p, 1, m) != ref["bits"]
+        in_window = bool(np.all(np.abs(ref["dots"][diff]) <= D * 2.0 ** -24 * ref["absdots"][diff]))
+        lo = (ref["norm64"] * (1 - 1e-6)).astype(np.float16)
+        hi = (ref["norm64"] * (1 + 1e-6)).astype(np.float16)
+        norm_ok = bool(np.all((dev_n == lo) | (dev_n == hi)))
+    dt_oracle = time.perf_counter() - t0
+    frac = float(diff.mean())
+    ok = in_window and norm_ok and frac <= max(1e-6, 1.0 / diff.size)
+    try:
+        import threadpoolctl
+        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    except Exception:
+        cores = os.cpu_count()
+    result = {
+        "metric": "encode+pack GB/s (fp16 in + packed out) and % of HBM peak; tokens/sec",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded counter-based generator; no dataset)",
+        "config": {"workload": f"{args.workload}: {w.note.split('; b=')[0]}; " + (
+            "1-bit sign code of the rotated vector + fp32 norm" if kind == "rabitq"
+            else f"1-bit sign sketch, m = {m} Gaussian rows (fp16) + fp16 norm"),
+            "shape": [B, H, S, D], "pool_tensors": P},
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(B * S / (us * 1e-6), 1), "encode_us_per_launch": round(us, 3),
+        "norm_bytes_per_launch_not_counted": n_vec * norm_bytes, "wall_s_timed_region": round(wall, 4),
+        "parity_recheck": {"vectors": int(len(idx)), "differing_bit_fraction": frac, "ok": bool(ok)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "kernel": kname},
+        "cpu_baseline": {"value": round(len(idx) * (D * 2 + out_bytes) / dt_oracle / 1e9, 6), "unit": "GB/s",
+                         "cores": cores, "kind": "oracle",
+                         "sample": f"{len(idx)} of {n_vec} vectors (strided), {dt_oracle:.1f} s wall, numpy oracle"},
+    }
+    if kind == "qjl":
+        result["mfma"] = {"flops_per_launch": 2 * n_vec * m * D,
+                          "tflops": round(2 * n_vec * m * D / (us * 1e-6) / 1e12, 1), "peak_fp16_tflops": 2500.0}
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
 
 
 def bench_attend(args) -> int:

@@ -158,6 +158,57 @@ kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed
                                  uint16_t* x_out, void* stream);
 
 /*
+ * kvq_rabitq_encode_pack - device. 1-bit sign codes of the rotated vector with its norm,
+ * in one pass (blog, "rvq" tag page, "A fusion this codebase had already proven out": a
+ * RaBitQ encoder that rotates, binarizes with y >= 0, packs the sign bits and writes the
+ * magnitude). Bit j of a vector is [y_j >= 0] for y = H diag(s) x (the rotation of
+ * kvq_rvq_encode_pack; the positive scale does not change a sign), so a zero vector gets
+ * every bit set. Bits are packed LSB-first, 32 per word: bit j at word j / 32, bit j % 32;
+ * bits past d are 0.
+ *   cb        from kvq_build_codebooks(d, 1, signs): only d and the signs are used;
+ *             bits != 1 is KVQ_ERR_SHAPE
+ *   packed    device uint32 [B, H, S_cap, ceil(d / 32)], 16-byte aligned
+ *   norms     device float32 [B, H, S_cap]: ||x|| (the magnitude)
+ *   other arguments and errors as for kvq_rvq_encode_pack
+ */
+kvq_status kvq_rabitq_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
+                                  int64_t B, int64_t H, int64_t S,
+                                  uint32_t* packed, float* norms,
+                                  int64_t S_cap, int64_t s_offset, void* stream);
+
+/*
+ * kvq_qjl_supported - host. KVQ_OK when kvq_qjl_encode_pack takes head dimension d and
+ * sketch size m: d in {32, 64, 128, 256}, m in {32, 64, 96, 128, 192, 256}, and the
+ * sketch (2 m d bytes) plus the kernel's key tiles fit 64 KiB of LDS (m <= 128 at
+ * d = 128, m <= 64 at d = 256). KVQ_ERR_SHAPE otherwise.
+ */
+kvq_status kvq_qjl_supported(int32_t d, int32_t m);
+
+/*
+ * kvq_qjl_encode_pack - device. The QJL key encoder (blog, "turboquant" tag page,
+ * "Kernel 4: QJL Encode"): for every key x the m signs of S x, bit j = [(S x)_j >= 0],
+ * packed LSB-first (bit j of the sequence at word j / 32, bit j % 32; the pages' byte k,
+ * bit i is bit 8k + i, the same bytes on a little-endian machine), and the key norm
+ * ||x|| rounded to fp16 (nearest-even). The dot products multiply the fp16 values exactly
+ * and sum them in float32 (matrix cores), so a sign may differ from that of the exact dot
+ * only when |exact| <= d * 2^-24 * sum_i |S_ji x_i|.
+ *   sketch    device fp16 [m, d], row-major, 16-byte aligned, owned by the caller
+ *   d, m      see kvq_qjl_supported
+ *   x         device fp16 [B, H, S, d], contiguous, 16-byte aligned
+ *   packed    device uint32 [B, H, S_cap, m / 32], 16-byte aligned
+ *   norms     device fp16 [B, H, S_cap], 2-byte aligned
+ *   S_cap, s_offset, stream as for kvq_rvq_encode_pack
+ * Errors: KVQ_ERR_SHAPE (unsupported d or m, negative sizes), KVQ_ERR_ARG (null pointer),
+ * KVQ_ERR_ALIGN, KVQ_ERR_RANGE (s_offset + S > S_cap, overflow), KVQ_ERR_DEVICE (launch
+ * error); all but the last are checked before any HIP call. B * H * S == 0 returns KVQ_OK
+ * without touching any pointer.
+ */
+kvq_status kvq_qjl_encode_pack(const uint16_t* sketch, int32_t d, int32_t m, const uint16_t* x,
+                               int64_t B, int64_t H, int64_t S,
+                               uint32_t* packed, uint16_t* norms,
+                               int64_t S_cap, int64_t s_offset, void* stream);
+
+/*
  * kvq_rvq_attend - device. Softmax attention of fp16 queries over a packed two-stage key
  * cache and value cache, without reconstructing either (blog, "turboquant" tag page,
  * "Kernel 5": keys decoded as c1[i1] + c2[i2] on the fly inside a FlashAttention-style

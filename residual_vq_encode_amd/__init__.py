@@ -13,7 +13,10 @@ tensors are not on a GPU, the calls raise.
 The lower-level calls kvq_rvq_encode_pack / kvq_rvq_unpack_decode mirror the C ABI
 (including S_cap / s_offset for writing into and reading from a preallocated cache);
 kvq_mse_encode_pack / kvq_mse_unpack_decode (and encode_mse / decode_mse) are the
-single-stage codec: stage 1 only, one code stream.
+single-stage codec: stage 1 only, one code stream. kvq_rabitq_encode_pack (encode_rabitq)
+writes 1-bit sign codes of the rotated vector with its norm; kvq_qjl_encode_pack
+(encode_qjl) writes the 1-bit sign sketch of S x for a caller's fp16 sketch matrix S with
+fp16 norms; kvq_rvq_attend (attend) is softmax attention over packed key/value caches.
 """
 from __future__ import annotations
 
@@ -24,8 +27,9 @@ from typing import Optional
 __all__ = [
     "KvqError", "Codebooks", "load", "library_path", "build_codebooks", "kvq_build_codebooks",
     "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_mse_encode_pack", "kvq_mse_unpack_decode",
-    "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_status_str", "encode", "decode", "encode_mse",
-    "decode_mse", "attend", "n_words",
+    "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_rabitq_encode_pack", "kvq_qjl_encode_pack",
+    "kvq_qjl_supported", "kvq_status_str", "encode", "decode", "encode_mse", "decode_mse", "encode_rabitq",
+    "encode_qjl", "attend", "n_words",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +105,13 @@ def load() -> ctypes.CDLL:
                                                    ctypes.POINTER(ctypes.c_int64)]
     lib.kvq_rvq_attend_workspace_size.restype = ctypes.c_int
     lib.kvq_status_str.argtypes = [ctypes.c_int]
+    lib.kvq_rabitq_encode_pack.argtypes = [ctypes.POINTER(Codebooks), ptr, i64, i64, i64, ptr, ptr, i64, i64, ptr]
+    lib.kvq_rabitq_encode_pack.restype = ctypes.c_int
+    lib.kvq_qjl_supported.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.kvq_qjl_supported.restype = ctypes.c_int
+    lib.kvq_qjl_encode_pack.argtypes = [ptr, ctypes.c_int32, ctypes.c_int32, ptr, i64, i64, i64, ptr, ptr, i64, i64,
+                                        ptr]
+    lib.kvq_qjl_encode_pack.restype = ctypes.c_int
     lib.kvq_status_str.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -324,3 +335,73 @@ def attend(q, kcache, vcache, cbk: Codebooks, cbv: Codebooks, S_kv: int, scale=N
     out = torch.empty_like(q)
     kvq_rvq_attend(cbk, cbv, q, kcache, vcache, S_kv, 1.0 / math.sqrt(d) if scale is None else scale, ws, out, stream)
     return out
+
+
+def kvq_rabitq_encode_pack(cb: Codebooks, x, packed, norms, s_offset: int = 0, stream=None) -> None:
+    """1-bit sign codes [y >= 0] of the rotated vector. cb: built with bits = 1 (only d and the
+    signs are used); x: fp16 [B, H, S, d] contiguous; packed: int32/uint32
+    [B, H, S_cap, ceil(d / 32)]; norms: float32 [B, H, S_cap]."""
+    import torch
+    _require_cuda(x, packed, norms)
+    if cb.bits != 1:
+        raise ValueError("the sign code takes codebooks built with bits = 1")
+    if x.dtype != torch.float16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, d = x.shape
+    if d != cb.d:
+        raise ValueError(f"x has d={d}, codebooks have d={cb.d}")
+    S_cap = packed.shape[2]
+    _check_stream(cb, "packed", packed, B, H, S_cap)
+    if tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32 or not norms.is_contiguous():
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    _check(load().kvq_rabitq_encode_pack(ctypes.byref(cb), _ptr(x), B, H, S, _ptr(packed), _ptr(norms), S_cap,
+                                         int(s_offset), _stream_handle(stream)), "kvq_rabitq_encode_pack")
+
+
+def encode_rabitq(x, cb: Codebooks, stream=None):
+    """Allocate outputs and write the 1-bit sign codes. Returns (packed, norms)."""
+    import torch
+    B, H, S, d = x.shape
+    p = torch.empty((B, H, S, cb.n_words), dtype=torch.int32, device=x.device)
+    norms = torch.empty((B, H, S), dtype=torch.float32, device=x.device)
+    kvq_rabitq_encode_pack(cb, x, p, norms, 0, stream)
+    return p, norms
+
+
+def kvq_qjl_supported(d: int, m: int) -> bool:
+    """Whether the sign-sketch encoder takes head dimension d and sketch size m (host call)."""
+    return load().kvq_qjl_supported(int(d), int(m)) == 0
+
+
+def kvq_qjl_encode_pack(sketch, x, packed, norms, s_offset: int = 0, stream=None) -> None:
+    """1-bit sign sketch. sketch: fp16 [m, d] contiguous; x: fp16 [B, H, S, d] contiguous;
+    packed: int32/uint32 [B, H, S_cap, m / 32] (bit j of the sequence = [(S x)_j >= 0]);
+    norms: fp16 [B, H, S_cap]. Writes token s at cache position s_offset + s."""
+    import torch
+    _require_cuda(sketch, x, packed, norms)
+    if sketch.dtype != torch.float16 or sketch.dim() != 2 or not sketch.is_contiguous():
+        raise ValueError("sketch must be a contiguous fp16 [m, d] tensor")
+    if x.dtype != torch.float16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp16 [B, H, S, d] tensor")
+    m, d = sketch.shape
+    B, H, S, dx = x.shape
+    if dx != d:
+        raise ValueError(f"x has d={dx}, the sketch has d={d}")
+    S_cap = packed.shape[2]
+    if tuple(packed.shape) != (B, H, S_cap, m // 32) or not packed.is_contiguous() or packed.element_size() != 4:
+        raise ValueError(f"packed must be a contiguous 32-bit integer tensor of shape {(B, H, S_cap, m // 32)}")
+    if tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float16 or not norms.is_contiguous():
+        raise ValueError(f"norms must be contiguous float16 {(B, H, S_cap)}")
+    _check(load().kvq_qjl_encode_pack(_ptr(sketch), int(d), int(m), _ptr(x), B, H, S, _ptr(packed), _ptr(norms),
+                                      S_cap, int(s_offset), _stream_handle(stream)), "kvq_qjl_encode_pack")
+
+
+def encode_qjl(x, sketch, stream=None):
+    """Allocate outputs and write the sign sketch. Returns (packed, norms)."""
+    import torch
+    B, H, S, d = x.shape
+    m = sketch.shape[0]
+    p = torch.empty((B, H, S, m // 32), dtype=torch.int32, device=x.device)
+    norms = torch.empty((B, H, S), dtype=torch.float16, device=x.device)
+    kvq_qjl_encode_pack(sketch, x, p, norms, 0, stream)
+    return p, norms

@@ -8,11 +8,14 @@
 
 #include "kvq.h"
 #include "params.h"
+#include "qjl_params.h"
 
 namespace kvq {
 hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream);
+hipError_t launch_qjl(const QjlArgs& a, int d, int m, hipStream_t stream);
+int64_t qjl_lds_need(int d, int m);
 }  // namespace kvq
 
 namespace {
@@ -175,6 +178,7 @@ kvq_status encode_pack(const kvq_codebooks* cb, int stages, const uint16_t* x, i
                        void* stream) {
   kvq_status st = check_codebooks(cb);
   if (st != KVQ_OK) return st;
+  if (stages == 0 && cb->bits != 1) return KVQ_ERR_SHAPE;
   int64_t n_vec = 0;
   st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
   if (st != KVQ_OK) return st;
@@ -247,6 +251,47 @@ extern "C" kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint3
                                             int64_t B, int64_t H, int64_t S_cap, int64_t s_offset, int64_t S,
                                             uint16_t* x_out, void* stream) {
   return unpack_decode(cb, 1, packed, nullptr, norms, B, H, S_cap, s_offset, S, x_out, stream);
+}
+
+extern "C" kvq_status kvq_rabitq_encode_pack(const kvq_codebooks* cb, const uint16_t* x, int64_t B, int64_t H,
+                                             int64_t S, uint32_t* packed, float* norms, int64_t S_cap,
+                                             int64_t s_offset, void* stream) {
+  return encode_pack(cb, 0, x, B, H, S, packed, nullptr, norms, S_cap, s_offset, stream);
+}
+
+// ------------------------------------------------------------------------------ QJL sketch
+
+extern "C" kvq_status kvq_qjl_supported(int32_t d, int32_t m) {
+  if (d != 32 && d != 64 && d != 128 && d != 256) return KVQ_ERR_SHAPE;
+  if (m != 32 && m != 64 && m != 96 && m != 128 && m != 192 && m != 256) return KVQ_ERR_SHAPE;
+  if (kvq::qjl_lds_need(d, m) > 65536) return KVQ_ERR_SHAPE;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_qjl_encode_pack(const uint16_t* sketch, int32_t d, int32_t m, const uint16_t* x,
+                                          int64_t B, int64_t H, int64_t S, uint32_t* packed, uint16_t* norms,
+                                          int64_t S_cap, int64_t s_offset, void* stream) {
+  kvq_status st = kvq_qjl_supported(d, m);
+  if (st != KVQ_OK) return st;
+  if (B < 0 || H < 0 || S < 0) return KVQ_ERR_SHAPE;
+  if (S_cap < 0 || s_offset < 0 || s_offset > S_cap || S > S_cap - s_offset) return KVQ_ERR_RANGE;
+  int64_t bh, n_vec, rows, words, elems, bytes;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, S, &n_vec) || !mul_ok(bh, S_cap, &rows) || !mul_ok(rows, m / 32, &words) ||
+      !mul_ok(words, 4, &bytes) || !mul_ok(n_vec, d, &elems) || !mul_ok(elems, 2, &bytes))
+    return KVQ_ERR_RANGE;
+  if ((n_vec + 31) / 32 > std::numeric_limits<int32_t>::max() / 2) return KVQ_ERR_RANGE;
+  if (n_vec == 0) return KVQ_OK;
+  if (sketch == nullptr || x == nullptr || packed == nullptr || norms == nullptr) return KVQ_ERR_ARG;
+  if (!aligned(sketch, 16) || !aligned(x, 16) || !aligned(packed, 16) || !aligned(norms, 2)) return KVQ_ERR_ALIGN;
+  kvq::QjlArgs a;
+  a.x = x;
+  a.sketch = sketch;
+  a.packed = packed;
+  a.norms = norms;
+  a.n_vec = n_vec;
+  a.map = row_map(S, S_cap, s_offset);
+  const hipError_t e = kvq::launch_qjl(a, d, m, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
 // ------------------------------------------------------------------------------ attention

@@ -74,7 +74,9 @@ __device__ __forceinline__ void codes_bucket(float nx, float ay, float K2, int j
 
 // STAGES = 2: the two-stage residual codec (both code streams); STAGES = 1: the single-stage
 // codec ("turboquant" tag page, "Kernel 3": rotate, then the nearest Gaussian Lloyd-Max
-// centroid), stream 1 only.
+// centroid), stream 1 only; STAGES = 0 (BITS = 1 only): the 1-bit sign code [y >= 0] of
+// the rotated vector with its norm ("rvq" tag page, "A fusion this codebase had already
+// proven out": rotate, binarize, pack and magnitude in one kernel), stream 1 only.
 template <int D, int BITS, bool CONTIG, int STAGES>
 __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kernel(const EncodeArgs a) {
   using G = Layout<D>;
@@ -86,6 +88,7 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   constexpr int HALFM1 = (1 << (BITS - 1)) - 1;
   constexpr int CSTREAM = 64 * C / 4 + 4;            // STAGED: dwords per code stream (+ read pad)
   constexpr bool TWO = STAGES == 2;                  // stage 2 computed and stored
+  static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ float4 t1s[BITS >= 3 ? kTab1Max : 1];
@@ -226,7 +229,9 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
         uint32_t u1 = 0, u2 = 0;
 #pragma unroll
         for (int j = jhi - 1; j >= jlo; --j) {  // highest code first: code jlo ends in bits [0, BITS)
-          const float nx = __builtin_fmaf(y[j], -K, 0.0f);
+          // STAGES = 0 takes +K: then the sign bit is [y_true < 0] (zeros of either sign give
+          // +0), and the word is complemented below to [y_true >= 0]
+          const float nx = __builtin_fmaf(y[j], STAGES == 0 ? K : -K, 0.0f);
           const float ax = __builtin_fabsf(nx);
           if constexpr (BITS == 1) {
             // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
@@ -282,6 +287,7 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
           u1 ^= n1 * static_cast<uint32_t>(HALFM1);
           u2 ^= n2 * static_cast<uint32_t>(HALFM1);
         }
+        if constexpr (STAGES == 0) u1 = ~u1 & ones;
         w1[w] = u1;
         w2[w] = u2;
         __builtin_amdgcn_sched_barrier(0);
@@ -509,6 +515,8 @@ static auto encode_fn(int bits, int stages) -> hipError_t (*)(const EncodeArgs&,
     switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 2) }
   } else if (stages == 1) {
     switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 1) }
+  } else if (stages == 0 && bits == 1) {
+    return launch_encode_t<D, 1, 0>;
   }
   return nullptr;
 }

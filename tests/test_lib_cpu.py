@@ -27,9 +27,9 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = kvq.load()
     names = _declared_functions()
-    assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_rvq_attend",
-                     "kvq_rvq_attend_workspace_size", "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode",
-                     "kvq_status_str"]
+    assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_qjl_encode_pack",
+                     "kvq_qjl_supported", "kvq_rabitq_encode_pack", "kvq_rvq_attend", "kvq_rvq_attend_workspace_size",
+                     "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.library_path()], capture_output=True, text=True).stdout
@@ -206,3 +206,46 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 128, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         kvq.encode(x, cb)
+
+
+def test_sign_code_host_checks():
+    """kvq_rabitq_encode_pack: bits must be 1; the shared size, pointer and alignment checks
+    run before any HIP call (no GPU here)."""
+    lib = kvq.load()
+    A = 1 << 20
+    cb1, cb2 = kvq.build_codebooks(128, 1), kvq.build_codebooks(128, 2)
+
+    def enc(cb=cb1, x=A, B=1, H=2, S=3, p=A, n=A, S_cap=3, s_off=0):
+        return lib.kvq_rabitq_encode_pack(None if cb is None else ctypes.byref(cb), x, B, H, S, p, n, S_cap, s_off,
+                                          None)
+
+    assert enc(cb=None) == -1
+    assert enc(cb=cb2) == -2
+    assert enc(B=-1) == -2
+    assert enc(S=4) == -4 and enc(s_off=1) == -4
+    assert enc(B=0) == 0 and enc(S=0) == 0
+    assert enc(x=None) == -1 and enc(p=None) == -1 and enc(n=None) == -1
+    assert enc(x=A + 2) == -3 and enc(p=A + 4) == -3 and enc(n=A + 2) == -3
+
+
+def test_qjl_host_checks():
+    """kvq_qjl_supported's shape table and kvq_qjl_encode_pack's checks before any HIP call."""
+    lib = kvq.load()
+    ok = {(d, m) for d in (32, 64, 128, 256) for m in (32, 64, 96, 128, 192, 256)
+          if 2 * m * d + (2 if d == 256 else 4) * 32 * d * 2 <= 65536}
+    assert (128, 128) in ok and (128, 192) not in ok and (256, 64) in ok and (64, 256) in ok
+    for d in (16, 32, 48, 64, 128, 256, 512):
+        for m in (0, 16, 32, 64, 96, 100, 128, 160, 192, 256, 512):
+            assert (lib.kvq_qjl_supported(d, m) == 0) == ((d, m) in ok), (d, m)
+            assert kvq.kvq_qjl_supported(d, m) == ((d, m) in ok)
+    A = 1 << 20
+
+    def enc(sk=A, d=128, m=128, x=A, B=1, H=2, S=3, p=A, n=A, S_cap=3, s_off=0):
+        return lib.kvq_qjl_encode_pack(sk, d, m, x, B, H, S, p, n, S_cap, s_off, None)
+
+    assert enc(d=96) == -2 and enc(m=100) == -2 and enc(m=256) == -2
+    assert enc(H=-1) == -2
+    assert enc(S_cap=2) == -4 and enc(s_off=1) == -4 and enc(s_off=-1) == -4
+    assert enc(B=0) == 0 and enc(S=0, S_cap=0) == 0
+    assert enc(sk=None) == -1 and enc(x=None) == -1 and enc(p=None) == -1 and enc(n=None) == -1
+    assert enc(sk=A + 8) == -3 and enc(x=A + 2) == -3 and enc(p=A + 4) == -3 and enc(n=A + 1) == -3
