@@ -178,9 +178,9 @@ kvq_status kvq_rabitq_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
 
 /*
  * kvq_qjl_supported - host. KVQ_OK when kvq_qjl_encode_pack takes head dimension d and
- * sketch size m: d in {32, 64, 128, 256}, m in {32, 64, 96, 128, 192, 256}, and the
- * sketch (2 m d bytes) plus the kernel's key tiles fit 64 KiB of LDS (m <= 128 at
- * d = 128, m <= 64 at d = 256). KVQ_ERR_SHAPE otherwise.
+ * sketch size m: d in {32, 64, 128, 256}, m a multiple of 32 in [32, 256], and the sketch
+ * (2 m d bytes) plus the kernel's key tiles fit the 160 KiB of LDS of one workgroup
+ * (every such m at d <= 128, m <= 192 at d = 256). KVQ_ERR_SHAPE otherwise.
  */
 kvq_status kvq_qjl_supported(int32_t d, int32_t m);
 

@@ -263,8 +263,8 @@ extern "C" kvq_status kvq_rabitq_encode_pack(const kvq_codebooks* cb, const uint
 
 extern "C" kvq_status kvq_qjl_supported(int32_t d, int32_t m) {
   if (d != 32 && d != 64 && d != 128 && d != 256) return KVQ_ERR_SHAPE;
-  if (m != 32 && m != 64 && m != 96 && m != 128 && m != 192 && m != 256) return KVQ_ERR_SHAPE;
-  if (kvq::qjl_lds_need(d, m) > 65536) return KVQ_ERR_SHAPE;
+  if (m < 32 || m > 256 || m % 32 != 0) return KVQ_ERR_SHAPE;
+  if (kvq::qjl_lds_need(d, m) > 160 * 1024) return KVQ_ERR_SHAPE;
   return KVQ_OK;
 }
 

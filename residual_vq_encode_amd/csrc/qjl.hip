@@ -10,7 +10,7 @@
 // S x for a tile of 32 keys is a dense [m x d] x [d x 32] product, so it runs on the matrix
 // cores: v_mfma_f32_32x32x16_f16 multiplies the fp16 operands exactly and accumulates in
 // float32. The tile is streamed into the wave's LDS buffer with direct-to-LDS 16-byte loads;
-// the sketch sits in LDS for the whole (persistent) block.
+// the sketch sits in LDS for the whole (persistent) block, one copy shared by its waves.
 //
 // MFMA layout (32x32x16): lane l supplies row l % 32 of the A block and column l % 32 of the
 // B block, each with the 8 k-values 8 (l / 32) + [0, 8) of the 16-wide k-step, and receives
@@ -33,11 +33,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kQjlTile = 32;  // keys per wave tile: the 32 columns of one MFMA block
 
-// Waves per block: each holds a tile of 32 keys (64 d bytes) in LDS next to the sketch.
+// Waves per block: each holds a tile of 32 keys (64 d bytes) in LDS next to the one copy
+// of the sketch the block shares. At d = 128, m = 128 a block takes 64 KiB, so two blocks
+// (two waves per SIMD) share a CU. Measured on the Llama-layer keys: 4 waves per block
+// 19.0 us, 8 waves 20.9 us, 16 waves (one block per CU) 19.7 us; the sketch held in
+// registers instead of LDS 20.6 us. The loads alone take 15.4 us and the arithmetic alone
+// 11-13 us, so the remaining loss is their imperfect overlap.
 template <int D>
 constexpr int qjl_waves() {
-  return D >= 256 ? 2 : 4;
+  return 4;
 }
+
+constexpr int64_t kQjlLdsMax = 160 * 1024;  // LDS per workgroup (and per CU) on gfx950
 
 // LDS chunk swizzle: chunk c of row r (a sketch row or a key of the tile) is stored at
 // position c ^ (r & mask), so the 32 rows an MFMA operand read touches spread over the
@@ -141,33 +148,37 @@ __global__ __launch_bounds__(qjl_waves<D>() * 64) void qjl_encode_kernel(const Q
     ss += __shfl_xor(ss, 32);
     const float nrm = __builtin_sqrtf(ss);
 
-    // S x on the matrix cores: MB independent accumulators, k-steps outermost
-    f32x16_t acc[MB];
+    // S x on the matrix cores, MBC M-blocks at a time (independent accumulators, k-steps
+    // outermost), then their signs: register j of M-block mb is sketch dimension
+    // 32 mb + 16 h + j. The sign bit of (value + 0) is [value < 0] (adding +0 turns a -0
+    // into +0, which counts as >= 0); the chain shifts the highest dimension in first so
+    // dimension j ends at bit j.
+    constexpr int MBC = MB % 2 == 0 ? 2 : 1;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int m0 = 0; m0 < MB; m0 += MBC) {
+      f32x16_t acc[MBC];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mb][j] = 0.f;
+      for (int i = 0; i < MBC; ++i)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const f16x8_t sa =
-            __builtin_bit_cast(f16x8_t, sk[(32 * mb + srow) * CPV + ((2 * ks + h) ^ (srow & SWM))]);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa, b[ks], acc[mb], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int i = 0; i < MBC; ++i) {
+          const f16x8_t sa =
+              __builtin_bit_cast(f16x8_t, sk[(32 * (m0 + i) + srow) * CPV + ((2 * ks + h) ^ (srow & SWM))]);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa, b[ks], acc[i], 0, 0, 0);
+        }
       }
-    }
-
-    // signs: register j of M-block mb is sketch dimension 32 mb + 16 h + j. The sign bit of
-    // (value + 0) is [value < 0] (adding +0 turns a -0 into +0, which counts as >= 0); the
-    // chain shifts the highest dimension in first so dimension j ends at bit j.
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      uint32_t u = 0;
+      for (int i = 0; i < MBC; ++i) {
+        uint32_t u = 0;
 #pragma unroll
-      for (int j = 15; j >= 0; --j) u = __builtin_amdgcn_alignbit(u, __float_as_uint(acc[mb][j] + 0.0f), 31);
-      const uint32_t hw = ~u & 0xFFFFu;
-      const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hw), 32));
-      words[mb] = h == 0 ? (hw | (other << 16)) : (other | (hw << 16));
+        for (int j = 15; j >= 0; --j) u = __builtin_amdgcn_alignbit(u, __float_as_uint(acc[i][j] + 0.0f), 31);
+        const uint32_t hw = ~u & 0xFFFFu;
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hw), 32));
+        words[m0 + i] = h == 0 ? (hw | (other << 16)) : (other | (hw << 16));
+      }
     }
     nrm16 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(nrm));
     row = v < nv ? cache_row<CONTIG>(a.map, v0, v) : -1;
@@ -192,11 +203,13 @@ static hipError_t launch_qjl_t(const QjlArgs& a, hipStream_t stream) {
   const void* f = a.map.contiguous ? reinterpret_cast<const void*>(&qjl_encode_kernel<D, MB, true>)
                                    : reinterpret_cast<const void*>(&qjl_encode_kernel<D, MB, false>);
   const int64_t lds = qjl_lds_bytes<D>(MB * 32);
-  static int cap[2] = {0, 0};  // resident blocks per CU, asked once per kernel
+  static int cap[2] = {0, 0};  // resident blocks on the device, asked once per kernel
   int& c = cap[a.map.contiguous ? 1 : 0];
   if (c == 0) {
     int per_cu = 0, dev = 0, cus = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, qjl_waves<D>() * 64, lds);
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, qjl_waves<D>() * 64, lds);
     if (e != hipSuccess) return e;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
@@ -212,14 +225,16 @@ static hipError_t launch_qjl_t(const QjlArgs& a, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_qjl_d(const QjlArgs& a, int m, hipStream_t stream) {
-  // m = 32 MB; the sketch and the tiles fit 64 KiB of LDS (checked on the host)
+  // m = 32 MB; the sketch and the tiles fit the LDS (checked on the host)
   switch (m / 32) {
     case 1: return launch_qjl_t<D, 1>(a, stream);
     case 2: return launch_qjl_t<D, 2>(a, stream);
-    case 3: if constexpr (qjl_lds_bytes<D>(96) <= 65536) return launch_qjl_t<D, 3>(a, stream); break;
-    case 4: if constexpr (qjl_lds_bytes<D>(128) <= 65536) return launch_qjl_t<D, 4>(a, stream); break;
-    case 6: if constexpr (qjl_lds_bytes<D>(192) <= 65536) return launch_qjl_t<D, 6>(a, stream); break;
-    case 8: if constexpr (qjl_lds_bytes<D>(256) <= 65536) return launch_qjl_t<D, 8>(a, stream); break;
+    case 3: return launch_qjl_t<D, 3>(a, stream);
+    case 4: return launch_qjl_t<D, 4>(a, stream);
+    case 5: if constexpr (qjl_lds_bytes<D>(160) <= kQjlLdsMax) return launch_qjl_t<D, 5>(a, stream); break;
+    case 6: if constexpr (qjl_lds_bytes<D>(192) <= kQjlLdsMax) return launch_qjl_t<D, 6>(a, stream); break;
+    case 7: if constexpr (qjl_lds_bytes<D>(224) <= kQjlLdsMax) return launch_qjl_t<D, 7>(a, stream); break;
+    case 8: if constexpr (qjl_lds_bytes<D>(256) <= kQjlLdsMax) return launch_qjl_t<D, 8>(a, stream); break;
     default: break;
   }
   return hipErrorInvalidValue;

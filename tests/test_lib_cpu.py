@@ -231,11 +231,14 @@ def test_sign_code_host_checks():
 def test_qjl_host_checks():
     """kvq_qjl_supported's shape table and kvq_qjl_encode_pack's checks before any HIP call."""
     lib = kvq.load()
-    ok = {(d, m) for d in (32, 64, 128, 256) for m in (32, 64, 96, 128, 192, 256)
-          if 2 * m * d + (2 if d == 256 else 4) * 32 * d * 2 <= 65536}
-    assert (128, 128) in ok and (128, 192) not in ok and (256, 64) in ok and (64, 256) in ok
+    # the sketch (2 m d bytes) and one 32-key tile per wave (4 waves) fit the 160 KiB of LDS
+    # of a gfx950 workgroup
+    ok = {(d, m) for d in (32, 64, 128, 256) for m in range(32, 257, 32)
+          if 2 * m * d + 4 * 32 * d * 2 <= 160 * 1024}
+    assert (128, 256) in ok and (256, 192) in ok and (256, 224) not in ok
+    assert (64, 256) in ok and (32, 256) in ok
     for d in (16, 32, 48, 64, 128, 256, 512):
-        for m in (0, 16, 32, 64, 96, 100, 128, 160, 192, 256, 512):
+        for m in (0, 16, 32, 64, 96, 100, 128, 160, 192, 224, 256, 288, 512):
             assert (lib.kvq_qjl_supported(d, m) == 0) == ((d, m) in ok), (d, m)
             assert kvq.kvq_qjl_supported(d, m) == ((d, m) in ok)
     A = 1 << 20
@@ -243,7 +246,7 @@ def test_qjl_host_checks():
     def enc(sk=A, d=128, m=128, x=A, B=1, H=2, S=3, p=A, n=A, S_cap=3, s_off=0):
         return lib.kvq_qjl_encode_pack(sk, d, m, x, B, H, S, p, n, S_cap, s_off, None)
 
-    assert enc(d=96) == -2 and enc(m=100) == -2 and enc(m=256) == -2
+    assert enc(d=96) == -2 and enc(m=100) == -2 and enc(d=256, m=224) == -2 and enc(m=288) == -2
     assert enc(H=-1) == -2
     assert enc(S_cap=2) == -4 and enc(s_off=1) == -4 and enc(s_off=-1) == -4
     assert enc(B=0) == 0 and enc(S=0, S_cap=0) == 0
