@@ -47,6 +47,13 @@ WORKLOADS = {
     "prefill_kv_b4": ("prefill_kv", 4, 2, 2),
     # the single-stage codec (stage 1 only, one code stream) on the Llama layer
     "llama_layer_mse": ("llama_layer", 2, 8, 1),
+    # 3 bits per stage: 10 codes per word, words straddle the lanes of a vector
+    "llama_layer_b3": ("llama_layer", 3, 8, 2),
+    # other head dimensions, same bytes as the Llama layer
+    "head_dim_64": ("head_dim_64", 2, 8, 2),
+    "head_dim_256": ("head_dim_256", 2, 8, 2),
+    "head_dim_512": ("head_dim_512", 2, 8, 2),
+    "head_dim_1024": ("head_dim_1024", 2, 8, 2),
 }
 # 1-bit sign codes of the Llama layer's keys: the RaBitQ-style code of the rotated vector
 # (D bits + fp32 norm per vector) and the QJL sketch with m = 128 rows (128 bits + fp16 norm)
@@ -279,7 +286,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded counter-based generator; no dataset)",
-        "config": {"workload": f"{args.workload}: {w.note}" + ("" if stages == 2 else "; single-stage codec"),
+        "config": {"workload": f"{args.workload}: {w.note.split('; b')[0]}; b={bits}"
+                               + ("" if stages == 2 else "; single-stage codec"),
                    "shape": [B, H, S, D], "bits": bits, "stages": stages,
                    "pool_tensors": P, "step": "encode+pack then unpack+decode of one tensor"},
         "pct_of_hbm_peak": round(100.0 * enc_gbps / HBM_PEAK_GBPS, 2),

@@ -40,37 +40,25 @@
 
 namespace kvq {
 
+// Compile-time integer, and a loop over [I, N) whose body sees the index as one (so code
+// that indexes register arrays with it stays fully unrolled).
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Residency targets (waves per SIMD); the register allocator is held to 512 / target VGPRs.
 constexpr int kEncodeWavesPerEU = 4;
 constexpr int kDecodeWavesPerEU = 4;
 
 // ------------------------------------------------------------------------------ encode
-
-// Stage-1 and stage-2 codes of one coordinate (bits >= 3, bucket tables), as the count of
-// boundaries below the value: the quantizers are symmetric, so the code is
-// half + m (value > 0) or half - 1 - m (value <= 0), m = number of positive thresholds
-// below the magnitude. nx = -y * unit1 (sign bit = [y > 0]); ay = |y'| for stage 2.
-template <int BITS>
-__device__ __forceinline__ void codes_bucket(float nx, float ay, float K2, int j1max, int j2max,
-                                             const float4* t1s, const float2* t2s, uint32_t* c1,
-                                             uint32_t* c2) {
-  constexpr uint32_t HALF = 1u << (BITS - 1);
-  const uint32_t p1 = __float_as_uint(nx) >> 31;
-  const float ax = __builtin_fabsf(nx);
-  const int j1 = static_cast<int>(__builtin_fminf(ax, static_cast<float>(j1max)));
-  const float4 e = t1s[j1];
-  const bool gt = ax > e.x;
-  const uint32_t m1 = __float_as_uint(e.y) + (gt ? 1u : 0u);
-  const float cm = gt ? e.w : e.z;
-  const float x2 = __builtin_fmaf(ay, K2, -cm);  // residual magnitude in stage-2 units
-  const uint32_t p2 = p1 ^ (__float_as_uint(x2) >> 31);
-  const float ax2 = __builtin_fabsf(x2);
-  const int j2 = static_cast<int>(__builtin_fminf(ax2, static_cast<float>(j2max)));
-  const float2 e2 = t2s[j2];
-  const uint32_t m2 = __float_as_uint(e2.y) + (ax2 > e2.x ? 1u : 0u);
-  *c1 = p1 ? HALF + m1 : HALF - 1u - m1;
-  *c2 = p2 ? HALF + m2 : HALF - 1u - m2;
-}
 
 // STAGES = 2: the two-stage residual codec (both code streams); STAGES = 1: the single-stage
 // codec ("turboquant" tag page, "Kernel 3": rotate, then the nearest Gaussian Lloyd-Max
@@ -84,16 +72,16 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   constexpr int EPW = 32 / BITS;                     // codes per word
   constexpr int NW = (D + EPW - 1) / EPW;            // words per vector per stream
   constexpr bool STAGED = BITS == 3 && L > 1;        // 10-code words straddle lanes
-  constexpr int NWL = STAGED ? (NW + L - 1) / L : (L == 1 ? NW : C / EPW);  // words stored per lane
+  // words stored per lane: STAGED lanes store the (3 or 4) words that start in their slice
+  constexpr int NWL = STAGED ? 4 : (L == 1 ? NW : C / EPW);
   constexpr int HALFM1 = (1 << (BITS - 1)) - 1;
-  constexpr int CSTREAM = 64 * C / 4 + 4;            // STAGED: dwords per code stream (+ read pad)
   constexpr bool TWO = STAGES == 2;                  // stage 2 computed and stored
   static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
+  static_assert(!STAGED || C == 32, "a 3-bit lane slice is 96 bits");
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ float4 t1s[BITS >= 3 ? kTab1Max : 1];
   __shared__ float2 t2s[BITS >= 3 ? kTab2Max : 1];
-  __shared__ uint32_t cstage[STAGED ? kWavesPerBlock : 1][STAGED ? STAGES * CSTREAM : 1];
   if constexpr (BITS >= 3) {
     for (int i = threadIdx.x; i < kTab1Max; i += kBlockThreads)
       t1s[i] = make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3]);
@@ -115,6 +103,11 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
   const int rbase = lane * CH + swz<CH>(lane);
   // the transform of lane q comes out multiplied by (-1)^popcount(q) (see cross_stage)
   const bool negated = (__builtin_popcount(q) & 1) != 0;
+  // STAGED: lane q's codes are bits [96 q, 96 q + 96) of the vector's code stream without the
+  // two spare bits of each word (word w = stream bits [30 w, 30 w + 30)). The lane stores the
+  // words that start in its slice: the first starts at bit o of the slice, 3 or 4 of them.
+  const int s_off = STAGED ? (30 - (96 * q) % 30) % 30 : 0;
+  const int s_word = STAGED ? (96 * q + s_off) / 30 : 0;
   // fp16 weights (s_2p, s_2p+1) of this lane's C/2 coordinate pairs: the rotation's signs
   uint32_t wt[C / 2];
 #pragma unroll
@@ -183,10 +176,9 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
       if constexpr (STAGED) {
 #pragma unroll
         for (int k = 0; k < NWL; ++k) {
-          const int w = q + L * k;
-          if (w < NW) {
-            __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + w);
-            if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
+          if (k < 3 || s_off == 0) {
+            __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + s_word + k);
+            if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + s_word + k);
           }
         }
       } else {
@@ -220,132 +212,137 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kerne
     float K = (n > 0.f) ? a.k_scale * __builtin_amdgcn_rcpf(n) : 0.f;  // v_rcp_f32: 1 ulp
     const float K2 = K * a.r12;
     if (negated) K = -K;
-    if constexpr (!STAGED) {
+    // Codes of this lane's coordinates [jlo, jhi) of both stages, LSB-first with code jlo in
+    // bits [0, BITS) (as one packed word holds them).
+    auto pack_range = [&](auto first, auto end, uint32_t& w1o, uint32_t& w2o) {
+      constexpr int jlo = decltype(first)::value, jhi = decltype(end)::value, cnt = jhi - jlo;
+      uint32_t u1 = 0, u2 = 0;
 #pragma unroll
-      for (int w = 0; w < NWL; ++w) {
-        const int jlo = w * EPW;
-        const int jhi = (w + 1) * EPW < C ? (w + 1) * EPW : C;
-        const int cnt = jhi - jlo;
-        uint32_t u1 = 0, u2 = 0;
-#pragma unroll
-        for (int j = jhi - 1; j >= jlo; --j) {  // highest code first: code jlo ends in bits [0, BITS)
-          // STAGES = 0 takes +K: then the sign bit is [y_true < 0] (zeros of either sign give
-          // +0), and the word is complemented below to [y_true >= 0]
-          const float nx = __builtin_fmaf(y[j], STAGES == 0 ? K : -K, 0.0f);
-          const float ax = __builtin_fabsf(nx);
-          if constexpr (BITS == 1) {
-            // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
-            u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
-            const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -a.cm2[0]);
-            u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
-          } else if constexpr (BITS == 2) {
-            // Unit 2/T1: bit 31 of NX is P = [y > 0], bit 30 is O = [|NX| >= 2] = [|y| >= T1].
-            u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 30);
-            // U = |NX| - 2 is |y| - T1 in units 2/T1. T1 is the midpoint of the two centroid
-            // magnitudes c0 < c1, so the residual magnitude |y| - c (c the nearer one) is
-            // sign(U) * (|U| T1/2 - h), h = (c1 - c0)/2. W = (|U| T1/2 - h) in stage-2 units
-            // 2/T2 = |U| r12 - cm2[0]: its bit 31 is sign(W), bit 30 is [|W| >= 2] = [|r| >= T2].
-            const float u = ax - 2.0f;
-            const float w = __builtin_fmaf(__builtin_fabsf(u), a.r12, -a.cm2[0]);
-            u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(w), 30);
-          } else {
-            // bucket tables: m = number of positive thresholds below |y|, in table units
-            u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
-            const int j1 = static_cast<int>(__builtin_fminf(ax, static_cast<float>(a.j1max)));
-            const float4 e = t1s[j1];
-            const bool gt = ax > e.x;
-            u1 = (u1 << (BITS - 1)) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
-            const float cm = gt ? e.w : e.z;
-            const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -cm);
-            u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
-            const float ax2 = __builtin_fabsf(x2);
-            const int j2 = static_cast<int>(__builtin_fminf(ax2, static_cast<float>(a.j2max)));
-            const float2 e2 = t2s[j2];
-            u2 = (u2 << (BITS - 1)) | (__float_as_uint(e2.y) + (ax2 > e2.x ? 1u : 0u));
-          }
-        }
-        // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
-        // Q = [residual magnitude < 0] for stage 2. Stage 2's sign is P2 = P1 xor Q (the
-        // residual of a non-positive y is the negated magnitude). A field with P = 0 counts
-        // downward from the middle: its low bits are (2^(BITS-1) - 1) - m = m xor
-        // (2^(BITS-1) - 1); at BITS = 2 that low bit is O xor P xor 1 from the [>= T] bit the
-        // alignbit stored.
-        const uint32_t ones = field_ones<BITS>(cnt);
-        const uint32_t hi = ones << (BITS - 1);
-        if constexpr (BITS == 2) {
-          // stage 2 holds (sign(W), [|W| >= 2]); its residual-magnitude sign is
-          // Q = sign(U) xor sign(W) with sign(U) = not O, so P2 = P xor not O xor sign(W)
-          u2 ^= ((u1 ^ (u1 >> 1) ^ ones) & ones) << 1;
-          u1 ^= ~(u1 >> 1) & ones;
-          u2 ^= ~(u2 >> 1) & ones;
+      for (int j = jhi - 1; j >= jlo; --j) {  // highest code first: code jlo ends in bits [0, BITS)
+        // STAGES = 0 takes +K: then the sign bit is [y_true < 0] (zeros of either sign give
+        // +0), and the word is complemented below to [y_true >= 0]
+        const float nx = __builtin_fmaf(y[j], STAGES == 0 ? K : -K, 0.0f);
+        const float ax = __builtin_fabsf(nx);
+        if constexpr (BITS == 1) {
+          // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
+          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
+          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -a.cm2[0]);
+          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
+        } else if constexpr (BITS == 2) {
+          // Unit 2/T1: bit 31 of NX is P = [y > 0], bit 30 is O = [|NX| >= 2] = [|y| >= T1].
+          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 30);
+          // U = |NX| - 2 is |y| - T1 in units 2/T1. T1 is the midpoint of the two centroid
+          // magnitudes c0 < c1, so the residual magnitude |y| - c (c the nearer one) is
+          // sign(U) * (|U| T1/2 - h), h = (c1 - c0)/2. W = (|U| T1/2 - h) in stage-2 units
+          // 2/T2 = |U| r12 - cm2[0]: its bit 31 is sign(W), bit 30 is [|W| >= 2] = [|r| >= T2].
+          const float u = ax - 2.0f;
+          const float w = __builtin_fmaf(__builtin_fabsf(u), a.r12, -a.cm2[0]);
+          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(w), 30);
         } else {
-          u2 ^= u1 & hi;
+          // bucket tables: m = number of positive thresholds below |y|, in table units
+          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
+          const int j1 = static_cast<int>(__builtin_fminf(ax, static_cast<float>(a.j1max)));
+          const float4 e = t1s[j1];
+          const bool gt = ax > e.x;
+          u1 = (u1 << (BITS - 1)) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
+          const float cm = gt ? e.w : e.z;
+          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -cm);
+          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
+          const float ax2 = __builtin_fabsf(x2);
+          const int j2 = static_cast<int>(__builtin_fminf(ax2, static_cast<float>(a.j2max)));
+          const float2 e2 = t2s[j2];
+          u2 = (u2 << (BITS - 1)) | (__float_as_uint(e2.y) + (ax2 > e2.x ? 1u : 0u));
         }
-        if constexpr (BITS >= 3) {
-          const uint32_t n1 = ~(u1 >> (BITS - 1)) & ones;
-          const uint32_t n2 = ~(u2 >> (BITS - 1)) & ones;
-          u1 ^= n1 * static_cast<uint32_t>(HALFM1);
-          u2 ^= n2 * static_cast<uint32_t>(HALFM1);
-        }
-        if constexpr (STAGES == 0) u1 = ~u1 & ones;
-        w1[w] = u1;
-        w2[w] = u2;
+      }
+      // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
+      // Q = [residual magnitude < 0] for stage 2. Stage 2's sign is P2 = P1 xor Q (the
+      // residual of a non-positive y is the negated magnitude). A field with P = 0 counts
+      // downward from the middle: its low bits are (2^(BITS-1) - 1) - m = m xor
+      // (2^(BITS-1) - 1); at BITS = 2 that low bit is O xor P xor 1 from the [>= T] bit the
+      // alignbit stored.
+      const uint32_t ones = field_ones<BITS>(cnt);
+      const uint32_t hi = ones << (BITS - 1);
+      if constexpr (BITS == 2) {
+        // stage 2 holds (sign(W), [|W| >= 2]); its residual-magnitude sign is
+        // Q = sign(U) xor sign(W) with sign(U) = not O, so P2 = P xor not O xor sign(W)
+        u2 ^= ((u1 ^ (u1 >> 1) ^ ones) & ones) << 1;
+        u1 ^= ~(u1 >> 1) & ones;
+        u2 ^= ~(u2 >> 1) & ones;
+      } else {
+        u2 ^= u1 & hi;
+      }
+      if constexpr (BITS >= 3) {
+        const uint32_t n1 = ~(u1 >> (BITS - 1)) & ones;
+        const uint32_t n2 = ~(u2 >> (BITS - 1)) & ones;
+        u1 ^= n1 * static_cast<uint32_t>(HALFM1);
+        u2 ^= n2 * static_cast<uint32_t>(HALFM1);
+      }
+      if constexpr (STAGES == 0) u1 = ~u1 & ones;
+      w1o = u1;
+      w2o = u2;
+    };
+    if constexpr (!STAGED) {
+      static_for<0, NWL>([&](auto wi) {
+        constexpr int w = decltype(wi)::value;
+        pack_range(Int<w * EPW>{}, Int<((w + 1) * EPW < C ? (w + 1) * EPW : C)>{}, w1[w], w2[w]);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     } else {
-      // 3-bit codes: one byte per code into LDS (lane l's C codes at bytes [C l, C l + C) of
-      // each stream, i.e. vector vl's codes at [D vl, D vl + D)), then lane q of a vector
-      // packs words q, q + L, ... from ten consecutive bytes each.
-      uint32_t* cs = cstage[wv];
+      // 3-bit codes, 32 per lane: each stream's codes go into the lane's 96-bit slice of the
+      // stream (code j at slice bits [3 j, 3 j + 3)): codes 0-9, 11-20 and 22-31 as three
+      // 30-bit groups, codes 10 and 21 across the dword boundaries. A word is the 30 bits
+      // starting at its offset, from two consecutive slice dwords (or the last one and the
+      // first dword of the next lane's slice; zero past the vector's end).
+      uint32_t g1[3], g2[3], c10[2], c21[2];
+      static_for<0, 3>([&](auto ki) {
+        constexpr int k = decltype(ki)::value;
+        pack_range(Int<11 * k>{}, Int<11 * k + 10>{}, g1[k], g2[k]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      pack_range(Int<10>{}, Int<11>{}, c10[0], c10[1]);
+      pack_range(Int<21>{}, Int<22>{}, c21[0], c21[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // lanes whose slice starts at a word boundary take other dword pairs for words 1 and 2;
+      // the choice is a bit-select with a lane mask (a ternary here becomes a branch)
+      const uint32_t at0 = s_off == 0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int d4 = 0; d4 < C / 4; ++d4) {
-        uint32_t b1 = 0, b2 = 0;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          const int j = 4 * d4 + i;
-          uint32_t c1, c2;
-          codes_bucket<BITS>(__builtin_fmaf(y[j], -K, 0.0f), __builtin_fabsf(y[j]), K2, a.j1max, a.j2max, t1s,
-                             t2s, &c1, &c2);
-          b1 = (b1 << 8) | c1;
-          b2 = (b2 << 8) | c2;
+      for (int st = 0; st < STAGES; ++st) {
+        const uint32_t ga = st == 0 ? g1[0] : g2[0], gb = st == 0 ? g1[1] : g2[1], gc = st == 0 ? g1[2] : g2[2];
+        const uint32_t d0 = ga | (c10[st] << 30);
+        const uint32_t d1 = (c10[st] >> 2) | (gb << 1) | (c21[st] << 31);
+        const uint32_t d2 = (c21[st] >> 1) | (gc << 2);
+        uint32_t nb = static_cast<uint32_t>(__shfl(static_cast<int>(d0), lane + 1));
+        if (q == L - 1) nb = 0u;
+        constexpr uint32_t M30 = 0x3FFFFFFFu;
+        const uint32_t e0 = __builtin_amdgcn_alignbit(d1, d0, s_off) & M30;
+        const uint32_t e1 = ((__builtin_amdgcn_alignbit(d1, d0, 30) & at0) |
+                             (__builtin_amdgcn_alignbit(d2, d1, s_off - 2) & ~at0)) & M30;
+        const uint32_t e2 = ((__builtin_amdgcn_alignbit(d2, d1, 28) & at0) |
+                             (__builtin_amdgcn_alignbit(nb, d2, s_off - 4) & ~at0)) & M30;
+        const uint32_t e3 = __builtin_amdgcn_alignbit(nb, d2, 26) & M30;  // stored only when s_off == 0
+        if (st == 0) {
+          w1[0] = e0; w1[1] = e1; w1[2] = e2; w1[3] = e3;
+        } else {
+          w2[0] = e0; w2[1] = e1; w2[2] = e2; w2[3] = e3;
         }
-        cs[lane * (C / 4) + d4] = b1;
-        if constexpr (TWO) cs[CSTREAM + lane * (C / 4) + d4] = b2;
       }
-      wave_lds_fence();
-#pragma unroll
-      for (int k = 0; k < NWL; ++k) {
-        const int w = q + L * k;
-        const int wc = w < NW ? w : NW - 1;           // lanes without a k-th word repeat the last
-        const int base = vl * D + 10 * wc;            // byte offset of the word's first code
-        const int s = (base & 3) * 8;                 // 0 or 16 (base is even)
-        const int cnt = D - 10 * wc < 10 ? D - 10 * wc : 10;
-        const uint32_t keep = cnt == 10 ? 0x3FFFFFFFu : (1u << (3 * cnt)) - 1u;
-#pragma unroll
-        for (int st = 0; st < STAGES; ++st) {
-          const uint32_t* p = cs + st * CSTREAM + (base >> 2);
-          const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
-          const uint32_t e0 = __builtin_amdgcn_alignbit(d1, d0, s);
-          const uint32_t e1 = __builtin_amdgcn_alignbit(d2, d1, s);
-          const uint32_t e2 = d2 >> s;
-          const uint32_t wd = (pack4x3(e0) | (pack4x3(e1) << 12) | (pack4x3(e2 & 0xFFFFu) << 24)) & keep;
-          if (st == 0) w1[k] = wd; else w2[k] = wd;
-        }
-      }
-      wave_lds_fence();
     }
     n_prev = n;
-    row_prev = (vl < nv) ? cache_row<CONTIG>(a.map, v0, vl) : -1;
+    {
+      // computed for every lane, then selected (a lane-dependent call site would split the
+      // loop body into branches and raise register pressure)
+      const int64_t r = cache_row<CONTIG>(a.map, v0, vl);
+      row_prev = (vl < nv) ? r : -1;
+    }
   }
   if (row_prev >= 0) {
     if (q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
     if constexpr (STAGED) {
 #pragma unroll
       for (int k = 0; k < NWL; ++k) {
-        const int w = q + L * k;
-        if (w < NW) {
-          __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + w);
-          if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + w);
+        if (k < 3 || s_off == 0) {
+          __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + s_word + k);
+          if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + s_word + k);
         }
       }
     } else {

@@ -222,6 +222,15 @@ WORKLOADS = {
                            (4,), 104, "prefill flush: keys and values [16,32,4096,128], per-token scales; b=4"),
     "decode_append": Workload("decode_append", (TensorSpec(256, 8, 2000, 128, "gauss", 6),), (2,), 106,
                               "2000 decode steps of [256,8,1,128] appended into S_cap=32768 caches; b=2"),
+    # other head dimensions at the Llama layer's byte size (67 MB of fp16 keys)
+    "head_dim_64": Workload("head_dim_64", (TensorSpec(1, 32, 16384, 64, "gauss", 8),), (2,), 108,
+                            "keys [1,32,16384,64] N(0,1); b=2"),
+    "head_dim_256": Workload("head_dim_256", (TensorSpec(1, 32, 4096, 256, "gauss", 9),), (2,), 109,
+                             "keys [1,32,4096,256] N(0,1); b=2"),
+    "head_dim_512": Workload("head_dim_512", (TensorSpec(1, 32, 2048, 512, "gauss", 10),), (2,), 110,
+                             "keys [1,32,2048,512] N(0,1); b=2"),
+    "head_dim_1024": Workload("head_dim_1024", (TensorSpec(1, 32, 1024, 1024, "gauss", 11),), (2,), 111,
+                              "keys [1,32,1024,1024] N(0,1); b=2"),
 }
 
 DECODE_APPEND_S_CAP = 32768

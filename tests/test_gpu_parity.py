@@ -212,30 +212,32 @@ def test_degenerate_inputs(d, bits, sign_kind):
 # ------------------------------------------------------------------------- cache windows
 
 @pytest.mark.parametrize("S,S_cap,s_offset", [(1, 7, 3), (5, 9, 4), (64, 200, 100), (100, 100, 0), (130, 300, 1)])
-def test_cache_window(S, S_cap, s_offset):
-    _say(f"cache window S={S} S_cap={S_cap} s_offset={s_offset}")
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_cache_window(S, S_cap, s_offset, bits):
+    _say(f"cache window S={S} S_cap={S_cap} s_offset={s_offset} bits={bits}")
     spec = synth.TensorSpec(3, 2, S, 128, "gauss", 55 + S)
     x = synth.tensor(spec, device=DEV)
     s = _signs(56, 128)
-    p1, p2, nrm = gu.gpu_encode(x, s, 2, S_cap=S_cap, s_offset=s_offset, fill=-1)
+    nw = kvq.n_words(128, bits)
+    p1, p2, nrm = gu.gpu_encode(x, s, bits, S_cap=S_cap, s_offset=s_offset, fill=-1)
     win = slice(s_offset, s_offset + S)
-    rep, ref = gu.judge(x.cpu().numpy().reshape(-1, 128), s, 2, gu.as_u32(p1[:, :, win]).reshape(-1, 8),
-                        gu.as_u32(p2[:, :, win]).reshape(-1, 8), nrm[:, :, win].cpu().numpy().reshape(-1))
+    rep, ref = gu.judge(x.cpu().numpy().reshape(-1, 128), s, bits, gu.as_u32(p1[:, :, win]).reshape(-1, nw),
+                        gu.as_u32(p2[:, :, win]).reshape(-1, nw), nrm[:, :, win].cpu().numpy().reshape(-1))
     assert rep.ok(gu.flip_cap(rep.n_codes), gu.NORM_REL_TOL), rep.summary()
     outside = torch.ones(S_cap, dtype=torch.bool)
     outside[win] = False
     assert bool((p1[:, :, outside] == -1).all()) and bool((p2[:, :, outside] == -1).all())
     assert bool(torch.isnan(nrm[:, :, outside]).all())
     # decode the window back (oracle words uploaded into a cache of the same geometry)
-    cb = kvq.build_codebooks(128, 2, s)
+    cb = kvq.build_codebooks(128, bits, s)
     c1 = torch.zeros_like(p1)
     c2 = torch.zeros_like(p2)
-    c1[:, :, win] = torch.from_numpy(ref["packed1"].view(np.int32)).reshape(3, 2, S, 8).to(DEV)
-    c2[:, :, win] = torch.from_numpy(ref["packed2"].view(np.int32)).reshape(3, 2, S, 8).to(DEV)
+    c1[:, :, win] = torch.from_numpy(ref["packed1"].view(np.int32)).reshape(3, 2, S, nw).to(DEV)
+    c2[:, :, win] = torch.from_numpy(ref["packed2"].view(np.int32)).reshape(3, 2, S, nw).to(DEV)
     out = torch.empty((3, 2, S, 128), dtype=torch.float16, device=DEV)
     kvq.kvq_rvq_unpack_decode(cb, c1, c2, None, out, s_offset=s_offset)
     torch.cuda.synchronize()
-    want = rvq.decode(ref["packed1"], ref["packed2"], None, s, gu.tables(128, 2)).astype(np.float64)
+    want = rvq.decode(ref["packed1"], ref["packed2"], None, s, gu.tables(128, bits)).astype(np.float64)
     assert np.max(np.abs(out.cpu().numpy().reshape(-1, 128).astype(np.float64) - want)) <= gu.DECODE_UNIT_ATOL
 
 
