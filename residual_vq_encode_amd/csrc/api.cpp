@@ -304,7 +304,9 @@ namespace {
 // chunks of a multiple of the lane layout's positions per wave iteration, enough of them that
 // the partial pass has about 2048 waves (several per SIMD; longer chunks amortise each wave's
 // query rotation and its final merge, and leave fewer partial results to combine), but at
-// least 8 iterations per chunk.
+// least 8 iterations per chunk and at most 4096 chunks.
+constexpr int64_t kMaxAttendSplits = 4096;  // chunks per query vector the combine kernel takes
+
 struct AttendPlan {
   int64_t n_q = 0;
   int32_t chunk = 0, n_splits = 0, nqw = 1;
@@ -328,12 +330,14 @@ kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv
   int64_t chunk = (S_kv + splits0 - 1) / splits0;
   chunk = (chunk + vw - 1) / vw * vw;
   if (chunk < 8 * vw) chunk = 8 * vw;
+  const int64_t min_chunk = (S_kv + kMaxAttendSplits - 1) / kMaxAttendSplits;  // the combine's limit
+  if (chunk < min_chunk) chunk = (min_chunk + vw - 1) / vw * vw;
   if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;
   const int64_t n_splits = (S_kv + chunk - 1) / chunk;
   int64_t units = 0, ws = 0;
   if (!mul_ok(n_q, n_splits, &units) || !mul_ok(units, (d + 4) * 4, &ws)) return KVQ_ERR_RANGE;
   if (units / nqw / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max() ||
-      n_q > std::numeric_limits<int32_t>::max())
+      n_q > std::numeric_limits<int32_t>::max() / 16)  // combine blocks: n_q * (d / 64)
     return KVQ_ERR_RANGE;
   p->n_q = n_q;
   p->chunk = static_cast<int32_t>(chunk);

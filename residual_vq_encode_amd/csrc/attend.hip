@@ -98,6 +98,23 @@ __device__ __forceinline__ void nibble_z(const uint32_t (&w1)[NWL], const uint32
   }
 }
 
+// The inverse rotation of this lane's slice in float32: z <- diag(s_v) H z / sqrt(D) for the
+// lane's C coordinates [C q, C q + C) (H in registers, then across the L lanes of the
+// vector; cross_stage leaves the lane's result multiplied by (-1)^popcount(q)). vsg holds
+// the value signs, bit c of word c / 32.
+template <int D, int CM>
+__device__ __forceinline__ void unrotate_f32(float (&z)[(Layout<D, CM>::C)], int q, float inv_sqrt_d,
+                                             const uint32_t* vsg) {
+  using G = Layout<D, CM>;
+  constexpr int C = G::C, LOG_L = G::LOG_L;
+  lane_stages<C, 1>(z);
+  cross_stages<C, LOG_L>(z, q);
+  const float K = (__builtin_popcount(q) & 1) ? -inv_sqrt_d : inv_sqrt_d;
+  const uint32_t sw = vsg[(C * q) >> 5] >> ((C * q) & 31);
+#pragma unroll
+  for (int j = 0; j < C; ++j) z[j] = __uint_as_float(__float_as_uint(z[j] * K) ^ (((sw >> j) & 1u) << 31));
+}
+
 // Coordinates per lane of the attention layout: 16 when a wave serves several queries
 // (their rotated queries and accumulators are 2 * NQW * C registers per lane), else 32.
 template <int D, int NQW>
@@ -122,7 +139,9 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   __shared__ __align__(16) float ztk[NT];
   __shared__ __align__(16) float ztv[NT];
   __shared__ uint32_t kx[D / 2];  // key signs as fp16 sign-bit masks, one word per coordinate pair
+  __shared__ uint32_t vsg[(D + 31) / 32];  // value signs, bit c of word c / 32
   __shared__ uint32_t cstage[S::STAGED ? kWavesPerBlock : 1][S::STAGED ? 2 * S::CSTREAM : 1];
+  for (int i = threadIdx.x; i < (D + 31) / 32; i += kBlockThreads) vsg[i] = a.vsign[i];
   if constexpr (P != 0) {
     fill_nibble_table<BITS>(a.ztab_k, ztk);
     fill_nibble_table<BITS>(a.ztab_v, ztv);
@@ -265,7 +284,8 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
       for (int j = 0; j < C; ++j) acc[k][j] = __builtin_fmaf(w[k], z[j], acc[k][j]);
   }
 
-  // 3. Merge the lane groups (lanes with equal q), then group 0 writes each query's state.
+  // 3. Merge the lane groups (lanes with equal q), rotate the accumulator back (every lane
+  //    group holds the merged state), then group 0 writes each query's record.
 #pragma unroll
   for (int k = 0; k < NQW; ++k) {
 #pragma unroll
@@ -278,6 +298,7 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
       for (int j = 0; j < C; ++j) acc[k][j] = acc[k][j] * f1 + __shfl_xor(acc[k][j], off) * f2;
       m[k] = M;
     }
+    unrotate_f32<D, CM>(acc[k], q, a.inv_sqrt_d, vsg);
     if (vl == 0) {
       float* ws = a.ws + (qv[k] * a.n_splits + sp) * (D + 4);
       if (q == 0) {
@@ -292,84 +313,83 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   }
 }
 
-// One block per query vector. The block's threads form SG groups; group g merges chunks
-// g, g + SG, ... with each thread owning D / (1024 / SG) coordinates, the groups meet in LDS,
-// and the first wave rotates the merged vector back with the codec's lane layout.
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 4096;  // chunks per query vector (the host plan keeps below this)
 
+// Coordinates per combine block.
+template <int D>
+constexpr int combine_slice() {
+  return D < 64 ? D : 64;
+}
+
+// One block per (query vector, slice of 64 coordinates), in two passes so that no load waits
+// on another: the chunks' maxima give M = max_s m_s, the weights f_s = 2^(m_s - M) (kept in
+// LDS) and S = sum_s f_s l_s; then thread t sums f_s u_s over the chunks s = t / Q4 mod G of
+// its coordinate quad t mod Q4 (Q4 quads in the slice, G = 256 / Q4 groups), the G partial
+// sums meet in LDS, and out = RN16(sum / S). The records u_s are already rotated back.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attend_combine(const AttendArgs a) {
-  using G = Layout<D>;
-  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, CH = G::CH;
-  constexpr int SG = D >= kCombineThreads ? 1 : kCombineThreads / D;  // split groups
-  constexpr int TPG = kCombineThreads / SG;                            // threads per group
-  constexpr int CPT = D / TPG;                                     // coordinates per thread
+  constexpr int SL = combine_slice<D>();
+  constexpr int Q4 = SL / 4;
+  constexpr int NG = kCombineThreads / Q4;
 
-  __shared__ uint32_t vx[D / 2];  // value signs as fp16 sign-bit masks
-  __shared__ float gm[SG], gs[SG];
-  __shared__ float ga[SG][D];
-  for (int m = threadIdx.x; m < D / 2; m += kCombineThreads) {
-    const uint32_t s0 = (a.vsign[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
-    const uint32_t s1 = (a.vsign[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
-    vx[m] = (s0 ? 0x8000u : 0u) | (s1 ? 0x80000000u : 0u);
-  }
-  const int64_t qv = blockIdx.x;
-  const int g = threadIdx.x / TPG, t = threadIdx.x % TPG;
+  __shared__ float fs[kMaxSplits];
+  __shared__ float red[2][kCombineThreads / 64];
+  __shared__ float4 pa[NG][Q4];
+  const int64_t qv = blockIdx.x / (D / SL);
+  const int c0 = static_cast<int>(blockIdx.x % (D / SL)) * SL;
+  const float* wq = a.ws + qv * a.n_splits * (D + 4);
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
 
-  // merge this group's chunks: M = max, sum = sum l 2^(m - M), A = sum acc 2^(m - M)
-  float M = -FLT_MAX, sum = 0.f, A[CPT];
+  // pass 1: M, the weights, S
+  float M = -FLT_MAX;
+  for (int sp = t; sp < a.n_splits; sp += kCombineThreads) M = __builtin_fmaxf(M, wq[sp * (D + 4)]);
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) A[i] = 0.f;
-#pragma unroll 4
-  for (int sp = g; sp < a.n_splits; sp += SG) {
-    const float* ws = a.ws + (qv * a.n_splits + sp) * (D + 4);
-    const float ms = ws[0], ls = ws[1];
-    const float Mn = __builtin_fmaxf(M, ms);
-    const float f1 = exp2_fast(M - Mn), f2 = exp2_fast(ms - Mn);
-    sum = sum * f1 + ls * f2;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) A[i] = A[i] * f1 + ws[4 + t * CPT + i] * f2;
-    M = Mn;
-  }
-  if (t == 0) {
-    gm[g] = M;
-    gs[g] = sum;
-  }
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) ga[g][t * CPT + i] = A[i];
+  for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[0][wv] = M;
   __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kCombineThreads / 64; ++k) M = __builtin_fmaxf(M, red[0][k]);
+  float S = 0.f;
+  for (int sp = t; sp < a.n_splits; sp += kCombineThreads) {
+    const float f = exp2_fast(wq[sp * (D + 4)] - M);
+    fs[sp] = f;
+    S += f * wq[sp * (D + 4) + 1];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  if (lane == 0) red[1][wv] = S;
+  __syncthreads();
+  S = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineThreads / 64; ++k) S += red[1][k];
 
-  // first wave: lanes q < L of lane group 0 own coordinates [C q, C q + C)
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int q = lane & (L - 1);
-    const int vl = lane >> LOG_L;
-    float Mt = -FLT_MAX;
-#pragma unroll
-    for (int k = 0; k < SG; ++k) Mt = __builtin_fmaxf(Mt, gm[k]);
-    float St = 0.f, z[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) z[j] = 0.f;
-#pragma unroll
-    for (int k = 0; k < SG; ++k) {
-      const float f = exp2_fast(gm[k] - Mt);
-      St += gs[k] * f;
-#pragma unroll
-      for (int j = 0; j < C; ++j) z[j] += ga[k][q * C + j] * f;
+  // pass 2: sum_s f_s u_s over this block's coordinates
+  const int qd = t % Q4, grp = t / Q4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int sp = grp; sp < a.n_splits; sp += NG) {
+    const float f = fs[sp];
+    const float4 v = reinterpret_cast<const float4*>(wq + sp * (D + 4) + 4 + c0)[qd];
+    acc.x = __builtin_fmaf(f, v.x, acc.x);
+    acc.y = __builtin_fmaf(f, v.y, acc.y);
+    acc.z = __builtin_fmaf(f, v.z, acc.z);
+    acc.w = __builtin_fmaf(f, v.w, acc.w);
+  }
+  pa[grp][qd] = acc;
+  __syncthreads();
+  if (t < Q4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int k = 0; k < NG; ++k) {
+      const float4 u = pa[k][t];
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
     }
-    // out = diag(s_v) H (A / sum) / sqrt(D), rounded to fp16
-    float K = a.inv_sqrt_d / St;
-    if (__builtin_popcount(q) & 1) K = -K;
-    uint32_t o[C / 2];
-    unrotate_f16<D>(z, K, q, o);
-    if (vl == 0) {
-      uint4* dst = reinterpret_cast<uint4*>(a.out + qv * D + q * C);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int p = q * (C / 2) + 4 * c;
-        dst[c] = make_uint4(o[4 * c] ^ vx[p], o[4 * c + 1] ^ vx[p + 1], o[4 * c + 2] ^ vx[p + 2], o[4 * c + 3] ^ vx[p + 3]);
-      }
-    }
+    const float r = 1.0f / S;
+    const half2_t h0 = {static_cast<_Float16>(v.x * r), static_cast<_Float16>(v.y * r)};
+    const half2_t h1 = {static_cast<_Float16>(v.z * r), static_cast<_Float16>(v.w * r)};
+    reinterpret_cast<uint2*>(a.out + qv * D + c0)[t] =
+        make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
   }
 }
 
@@ -380,12 +400,13 @@ static hipError_t launch_attend_t(const AttendArgs& a, hipStream_t stream) {
   void* args[] = {const_cast<AttendArgs*>(&a)};
   const int64_t units = (a.n_q / NQW) * a.n_splits;
   const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > INT_MAX || a.n_q > INT_MAX) return hipErrorInvalidValue;
+  if (blocks > INT_MAX || a.n_q * (D / combine_slice<D>()) > INT_MAX) return hipErrorInvalidValue;
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attend_partial<D, BITS, NQW>),
                                  dim3(static_cast<int>(blocks)), dim3(kBlockThreads), args, 0, stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_combine<D>), dim3(static_cast<int>(a.n_q)),
-                         dim3(kCombineThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_combine<D>),
+                         dim3(static_cast<int>(a.n_q * (D / combine_slice<D>()))), dim3(kCombineThreads), args, 0,
+                         stream);
 }
 
 template <int D, int BITS>

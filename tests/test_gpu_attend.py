@@ -104,6 +104,12 @@ def test_attend_llama_decode_step():
     _check(128, 2, B=1, Hq=32, Hkv=8, Sq=1, S_cap=8192, S_kv=8192, seed=8)
 
 
+def test_attend_long_context_many_chunks():
+    """One query over 300k positions: about 1900 chunks meet in the combine pass."""
+    _say("attend long context S_kv=300000 d=64")
+    _check(64, 2, B=1, Hq=1, Hkv=1, Sq=1, S_cap=300000, S_kv=299999, seed=9)
+
+
 def test_attend_ignores_positions_past_s_kv_and_is_deterministic():
     d, bits, S_cap, S_kv = 128, 2, 200, 150
     sk = synth.signs(1, d).numpy()

@@ -189,13 +189,16 @@ def test_attend_host_side_argument_checks():
     for (d, B, Hq, Sq, Hkv, S_kv, nqw) in ((128, 1, 32, 1, 8, 32768, 4), (128, 1, 1, 1, 1, 5, 1),
                                            (128, 4, 8, 3, 4, 1000, 2), (128, 1, 32, 1, 32, 1, 1),
                                            (64, 2, 6, 1, 2, 700, 1), (1024, 1, 8, 1, 2, 3000, 1),
-                                           (16, 1, 4, 2, 1, 77, 4)):
+                                           (16, 1, 4, 2, 1, 77, 4), (128, 1, 1, 1, 1, 10 ** 7, 1)):
         nq = B * Hq * Sq
         cm = 16 if nqw > 1 and d >= 32 else 32
         vw = 64 // (d // min(d, cm))
         splits0 = -(-2048 * nqw // nq)
         chunk = -(-S_kv // splits0)
         chunk = max(-(-chunk // vw) * vw, 8 * vw)
+        min_chunk = -(-S_kv // 4096)
+        if chunk < min_chunk:
+            chunk = -(-min_chunk // vw) * vw
         n_splits = -(-S_kv // chunk)
         assert kvq.kvq_rvq_attend_workspace_size(d, B, Hq, Sq, Hkv, S_kv) == nq * n_splits * (d + 4) * 4
 
