@@ -452,7 +452,7 @@ def bench_attend(args) -> int:
     vcs = [dev_cache(5 + 1000 * i, cbv) for i in range(P)]
     qs = [synth.tensor(synth.TensorSpec(B, Hq, Sq, D, "gauss", 77 + i), device=dev) for i in range(P)]
     outs = [torch.empty_like(qs[0]) for _ in range(P)]
-    ws = torch.empty(kvq.kvq_rvq_attend_workspace_size(D, B, Hq, Sq, Hkv, S) // 4 + 4, dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_rvq_attend_workspace_size(D, bits, B, Hq, Sq, Hkv, S) // 4 + 4, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(D)
 
     def run(j):
@@ -472,7 +472,10 @@ def bench_attend(args) -> int:
     wall = time.perf_counter() - wall0
     us = e0.elapsed_time(e1) * 1e3 / K
     gq = (Hq // Hkv) * Sq  # query vectors per key/value head; a wave serves nqw of them
-    nqw = 4 if gq % 4 == 0 and D <= 512 else 2 if gq % 2 == 0 and D <= 512 else 1
+    if D in (64, 128) and bits != 3 and D * bits >= 128:
+        nqw = 16  # the matrix-core pass
+    else:
+        nqw = 4 if gq % 4 == 0 and D <= 512 else 2 if gq % 2 == 0 and D <= 512 else 1
     cache_bytes = B * Hkv * S * 2 * (2 * nw * 4 + 4)
     alg = cache_bytes + 2 * B * Hq * Sq * D * 2
     gbps = alg / (us * 1e-6) / 1e9
@@ -513,7 +516,8 @@ def bench_attend(args) -> int:
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": alg,
-                     "kernel": f"kvq::attend_partial<{D}, {bits}, {nqw}> + attend_combine<{D}>"},
+                     "kernel": (f"kvq::attend_mfma<{D}, {bits}>" if nqw == 16 else f"kvq::attend_partial<{D}, {bits}, {nqw}>")
+                               + f" + attend_combine<{D}>"},
         "cpu_baseline": {"value": round(alg / dt_oracle / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
                          "sample": f"the whole step ({B * Hq * Sq} query vectors over {S} positions), "
                                    f"{dt_oracle:.1f} s wall, numpy float64 oracle"},

@@ -245,11 +245,11 @@ kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, co
 
 /*
  * kvq_rvq_attend_workspace_size - host. Workspace bytes kvq_rvq_attend needs for these
- * sizes (d as in the codebooks; B, Hq, Sq, Hkv, S_kv as passed to kvq_rvq_attend).
- * Errors: KVQ_ERR_ARG (bytes NULL), KVQ_ERR_SHAPE (d not a power of two in range, negative
- * sizes, Hq not a multiple of Hkv), KVQ_ERR_RANGE (S_kv < 1 or overflow).
+ * sizes (d and bits as in the codebooks; B, Hq, Sq, Hkv, S_kv as passed to kvq_rvq_attend).
+ * Errors: KVQ_ERR_ARG (bytes NULL), KVQ_ERR_SHAPE (d not a power of two in range, bits out
+ * of range, negative sizes, Hq not a multiple of Hkv), KVQ_ERR_RANGE (S_kv < 1 or overflow).
  */
-kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
+kvq_status kvq_rvq_attend_workspace_size(int32_t d, int32_t bits, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
                                          int64_t S_kv, int64_t* bytes);
 
 /* Static text for a status code; never NULL. */

@@ -101,7 +101,7 @@ def load() -> ctypes.CDLL:
     lib.kvq_rvq_attend.argtypes = [ctypes.POINTER(Codebooks), ctypes.POINTER(Codebooks), ptr, i64, i64, i64, i64,
                                    ptr, ptr, ptr, ptr, ptr, ptr, i64, i64, ctypes.c_float, ptr, i64, ptr, ptr]
     lib.kvq_rvq_attend.restype = ctypes.c_int
-    lib.kvq_rvq_attend_workspace_size.argtypes = [ctypes.c_int32, i64, i64, i64, i64, i64,
+    lib.kvq_rvq_attend_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, i64, i64, i64, i64, i64,
                                                    ctypes.POINTER(ctypes.c_int64)]
     lib.kvq_rvq_attend_workspace_size.restype = ctypes.c_int
     lib.kvq_status_str.argtypes = [ctypes.c_int]
@@ -288,10 +288,10 @@ def decode_mse(packed, norms, cb: Codebooks, stream=None):
     return out
 
 
-def kvq_rvq_attend_workspace_size(d: int, B: int, Hq: int, Sq: int, Hkv: int, S_kv: int) -> int:
+def kvq_rvq_attend_workspace_size(d: int, bits: int, B: int, Hq: int, Sq: int, Hkv: int, S_kv: int) -> int:
     """Workspace bytes kvq_rvq_attend needs (host call)."""
     out = ctypes.c_int64(0)
-    _check(load().kvq_rvq_attend_workspace_size(int(d), int(B), int(Hq), int(Sq), int(Hkv), int(S_kv),
+    _check(load().kvq_rvq_attend_workspace_size(int(d), int(bits), int(B), int(Hq), int(Sq), int(Hkv), int(S_kv),
                                                 ctypes.byref(out)),
            "kvq_rvq_attend_workspace_size")
     return out.value
@@ -330,7 +330,8 @@ def attend(q, kcache, vcache, cbk: Codebooks, cbv: Codebooks, S_kv: int, scale=N
     import torch
     B, Hq, Sq, d = q.shape
     Hkv = kcache[0].shape[1]
-    ws = torch.empty(max(16, kvq_rvq_attend_workspace_size(d, B, Hq, Sq, Hkv, S_kv)) // 4, dtype=torch.float32,
+    ws = torch.empty(max(16, kvq_rvq_attend_workspace_size(d, cbk.bits, B, Hq, Sq, Hkv, S_kv)) // 4,
+                     dtype=torch.float32,
                      device=q.device)
     out = torch.empty_like(q)
     kvq_rvq_attend(cbk, cbv, q, kcache, vcache, S_kv, 1.0 / math.sqrt(d) if scale is None else scale, ws, out, stream)

@@ -298,13 +298,17 @@ extern "C" kvq_status kvq_qjl_encode_pack(const uint16_t* sketch, int32_t d, int
 
 namespace {
 
-// How the attention splits its work. A wave serves nqw query vectors that read the same
-// key/value head (the largest of 4, 2, 1 that divides the query vectors per head; 1 at
-// d = 1024, where their state does not fit the registers). The cached positions are cut into
-// chunks of a multiple of the lane layout's positions per wave iteration, enough of them that
-// the partial pass has about 2048 waves (several per SIMD; longer chunks amortise each wave's
-// query rotation and its final merge, and leave fewer partial results to combine), but at
-// least 8 iterations per chunk and at most 4096 chunks.
+// How the attention splits its work. With d = 64 or 128 and b = 1, 2 or 4 (d b >= 128) the
+// partial pass runs on the matrix cores: a wave serves 16 query vectors of one key/value
+// head (nqw = 16; the query vectors of a head are cut into groups of 16, the last one
+// padded) and takes 32 cached positions per iteration. Otherwise a wave serves nqw query
+// vectors of a head (the largest of 4, 2, 1 that divides the query vectors per head; 1 at
+// d = 1024, where their state does not fit the registers) and a multiple of the lane
+// layout's positions per iteration. The cached positions are cut into chunks of whole
+// iterations, enough of them that the partial pass has about 2048 waves (several per SIMD;
+// longer chunks amortise each wave's query rotation and its final merge, and leave fewer
+// partial results to combine), at least 4 (matrix path) or 8 iterations per chunk, and at
+// most 4096 chunks.
 constexpr int64_t kMaxAttendSplits = 4096;  // chunks per query vector the combine kernel takes
 
 struct AttendPlan {
@@ -313,30 +317,49 @@ struct AttendPlan {
   int64_t ws_bytes = 0;
 };
 
-kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, int64_t S_kv, AttendPlan* p) {
+bool attend_on_matrix_cores(int32_t d, int32_t bits) {
+  return (d == 64 || d == 128) && bits != 3 && d * bits >= 128;
+}
+
+kvq_status attend_plan(int32_t d, int32_t bits, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, int64_t S_kv,
+                       AttendPlan* p) {
   if (d < KVQ_MIN_D || d > KVQ_MAX_D || !is_pow2(d)) return KVQ_ERR_SHAPE;
+  if (bits < 1 || bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
   if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 0) return KVQ_ERR_SHAPE;
   if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return KVQ_ERR_SHAPE;
   if (S_kv < 1 || S_kv > (int64_t(1) << 40)) return KVQ_ERR_RANGE;
   int64_t bh = 0, n_q = 0, gq = 0;
   if (!mul_ok(B, Hq, &bh) || !mul_ok(bh, Sq, &n_q)) return KVQ_ERR_RANGE;
   if (Hq > 0 && !mul_ok(Hq / Hkv, Sq, &gq)) return KVQ_ERR_RANGE;
+  const bool mat = attend_on_matrix_cores(d, bits);
   int nqw = 1;
-  if (d <= 512) nqw = gq % 4 == 0 ? 4 : gq % 2 == 0 ? 2 : 1;
-  const int64_t cm = (nqw > 1 && d >= 32) ? 16 : 32;  // coordinates per lane
-  const int64_t c = d < cm ? d : cm, vw = 64 / (d / c);
+  int64_t vw = 0, min_iters = 8, waves_per_split = 0;  // positions per iteration
+  if (mat) {
+    nqw = 16;
+    vw = 32;
+    min_iters = 4;
+    waves_per_split = gq > 0 ? (n_q / gq) * ((gq + 15) / 16) : 0;
+  } else {
+    if (d <= 512) nqw = gq % 4 == 0 ? 4 : gq % 2 == 0 ? 2 : 1;
+    const int64_t cm = (nqw > 1 && d >= 32) ? 16 : 32;  // coordinates per lane
+    const int64_t c = d < cm ? d : cm;
+    vw = 64 / (d / c);
+    waves_per_split = n_q / nqw;
+  }
   const int64_t want_waves = 2048;
-  const int64_t splits0 = n_q > 0 ? (want_waves * nqw + n_q - 1) / n_q : 1;
+  const int64_t splits0 = waves_per_split > 0 ? (want_waves + waves_per_split - 1) / waves_per_split : 1;
   int64_t chunk = (S_kv + splits0 - 1) / splits0;
   chunk = (chunk + vw - 1) / vw * vw;
-  if (chunk < 8 * vw) chunk = 8 * vw;
+  if (chunk < min_iters * vw) chunk = min_iters * vw;
   const int64_t min_chunk = (S_kv + kMaxAttendSplits - 1) / kMaxAttendSplits;  // the combine's limit
   if (chunk < min_chunk) chunk = (min_chunk + vw - 1) / vw * vw;
   if (chunk > (int64_t(1) << 30)) chunk = int64_t(1) << 30;
   const int64_t n_splits = (S_kv + chunk - 1) / chunk;
-  int64_t units = 0, ws = 0;
-  if (!mul_ok(n_q, n_splits, &units) || !mul_ok(units, (d + 4) * 4, &ws)) return KVQ_ERR_RANGE;
-  if (units / nqw / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max() ||
+  int64_t units = 0, ws = 0, waves = 0;
+  if (!mul_ok(n_q, n_splits, &units) || !mul_ok(units, (d + 4) * 4, &ws) ||
+      !mul_ok(waves_per_split, n_splits, &waves))
+    return KVQ_ERR_RANGE;
+  if (waves / kvq::kWavesPerBlock > std::numeric_limits<int32_t>::max() ||
       n_q > std::numeric_limits<int32_t>::max() / 16)  // combine blocks: n_q * (d / 64)
     return KVQ_ERR_RANGE;
   p->n_q = n_q;
@@ -349,11 +372,11 @@ kvq_status attend_plan(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv
 
 }  // namespace
 
-extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
-                                                    int64_t S_kv, int64_t* bytes) {
+extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int32_t bits, int64_t B, int64_t Hq, int64_t Sq,
+                                                    int64_t Hkv, int64_t S_kv, int64_t* bytes) {
   if (bytes == nullptr) return KVQ_ERR_ARG;
   AttendPlan p;
-  const kvq_status st = attend_plan(d, B, Hq, Sq, Hkv, S_kv, &p);
+  const kvq_status st = attend_plan(d, bits, B, Hq, Sq, Hkv, S_kv, &p);
   if (st != KVQ_OK) return st;
   *bytes = p.ws_bytes;
   return KVQ_OK;
@@ -377,7 +400,7 @@ extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codeboo
     return KVQ_ERR_RANGE;
   if (S_kv < 1 || S_cap < S_kv) return KVQ_ERR_RANGE;
   AttendPlan p;
-  st = attend_plan(cbk->d, B, Hq, Sq, Hkv, S_kv, &p);
+  st = attend_plan(cbk->d, cbk->bits, B, Hq, Sq, Hkv, S_kv, &p);
   if (st != KVQ_OK) return st;
   // the caches: [B, Hkv, S_cap, n_words] words and [B, Hkv, S_cap] norms must be addressable
   int64_t rows = 0, words = 0, bytes = 0;

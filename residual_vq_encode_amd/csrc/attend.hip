@@ -313,6 +313,451 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   }
 }
 
+// ------------------------------------------------------------------- matrix-core partial pass
+
+// The same partial results on the matrix cores (d = 64 or 128, b = 1, 2 or 4). One wave takes
+// up to 16 query vectors of one key/value head over one chunk, 32 cached positions per
+// iteration, with v_mfma_f32_16x16x32_f16:
+//   scores^T [32 positions x 16 queries] = Z_k [32 x d] . Q^T [d x 16]   (two 16-row blocks)
+//   out^T [d x 16 queries] += Z_v^T [d x 32] . P^T [32 x 16]
+// Every float32 operand is split into fp16 hi + lo (hi = RN16(v), lo = RN16(v - hi), their
+// sum within 2^-22 |v| of v) and a product takes three MFMAs (hi.hi + hi.lo + lo.hi), so the
+// scores and sums carry float32-level error. Rows of the score product are keys: lane l
+// supplies key l % 16 of the block with coordinates (d/4) (l / 16) + 8 s + [0, 8) at k-step s
+// (the same coordinate order in both operands), decoded straight from the packed words
+// through an LDS table of (hi, lo) pairs indexed by one nibble of each code stream. It
+// receives the scores of keys 4 (l / 16) + [0, 4) for query l % 16, which after the softmax
+// are exactly the lane's own P^T operand of the value product. The values are decoded the
+// same way into an LDS tile [32 keys][d] (hi and lo planes) and read back transposed with
+// ds_read_b64_tr_b16, which hands lane l coordinate l % 16 of four consecutive keys.
+// Queries are rotated once per wave (in the codec's lane layout), divided by their largest
+// coordinate so their fp16 parts cannot overflow; the value weights p n_v are kept against
+// their own softmax-style reference for the same reason, and both are put back in float32.
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaKeys = 32;  // cached positions per iteration
+constexpr int kMfmaQ = 16;     // query vectors per wave
+
+// fp16 hi + lo parts of v, packed in pairs: (hi(v0) | hi(v1) << 16) and the same for lo.
+__device__ __forceinline__ uint2 split_pair(float v0, float v1) {
+  const half2_t h = {static_cast<_Float16>(v0), static_cast<_Float16>(v1)};
+  const half2_t lo = {static_cast<_Float16>(v0 - static_cast<float>(h[0])),
+                      static_cast<_Float16>(v1 - static_cast<float>(h[1]))};
+  return make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, lo));
+}
+
+// Table of the matrix path: entry e (a nibble of each stream, P = 4 / b coordinates) holds the
+// fp16 hi parts of the P values c1[i1] + c2[i2] (in pairs, P / 2 words) then their lo parts;
+// at P = 1 one word, hi | lo << 16.
+template <int BITS>
+__device__ __forceinline__ void fill_mfma_table(const float* zt, uint32_t* tab) {
+  constexpr int P = 4 / BITS;
+  constexpr uint32_t M = (1u << BITS) - 1u;
+  for (int e = threadIdx.x; e < 256; e += kBlockThreads) {
+    float z[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const uint32_t i1 = (e >> (BITS * p)) & M, i2 = ((e >> 4) >> (BITS * p)) & M;
+      z[p] = zt[(i1 << BITS) | i2];
+    }
+    if constexpr (P == 1) {
+      const uint2 hl = split_pair(z[0], 0.f);
+      tab[e] = (hl.x & 0xFFFFu) | (hl.y << 16);
+    } else {
+#pragma unroll
+      for (int p = 0; p < P; p += 2) {
+        const uint2 hl = split_pair(z[p], z[p + 1]);
+        tab[e * P + p / 2] = hl.x;
+        tab[e * P + P / 2 + p / 2] = hl.y;
+      }
+    }
+  }
+}
+
+// The nibble bytes of a lane's words: byte k of lo[w] indexes coordinates of nibble 2k of
+// word w (stage 1 low, stage 2 high), of hi[w] nibble 2k + 1.
+template <int NWG>
+__device__ __forceinline__ void nibble_bytes(const uint32_t (&w1)[NWG], const uint32_t (&w2)[NWG], uint32_t (&lo)[NWG],
+                                             uint32_t (&hi)[NWG]) {
+#pragma unroll
+  for (int w = 0; w < NWG; ++w) {
+    lo[w] = (w1[w] & 0x0F0F0F0Fu) | ((w2[w] << 4) & 0xF0F0F0F0u);
+    hi[w] = ((w1[w] >> 4) & 0x0F0F0F0Fu) | (w2[w] & 0xF0F0F0F0u);
+  }
+}
+
+// The fp16 hi and lo parts of the lane's coordinates 8 S .. 8 S + 7 (of its slice), packed
+// as 8 halfs each (one MFMA operand).
+template <int BITS, int NWG, int S>
+__device__ __forceinline__ void table_operand(const uint32_t (&lo)[NWG], const uint32_t (&hi)[NWG],
+                                              const uint32_t* tab, u32x4_t& oh, u32x4_t& ol) {
+  constexpr int P = 4 / BITS;
+  constexpr int N0 = S * 8 / P;  // first nibble of the step
+  auto idx = [&](int t) -> uint32_t { return (((t & 1) ? hi[t >> 3] : lo[t >> 3]) >> (8 * ((t & 7) >> 1))) & 0xFFu; };
+  if constexpr (P == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint2 e = reinterpret_cast<const uint2*>(tab)[idx(N0 + k)];
+      oh[k] = e.x;
+      ol[k] = e.y;
+    }
+  } else if constexpr (P == 4) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint4 e = reinterpret_cast<const uint4*>(tab)[idx(N0 + k)];
+      oh[2 * k] = e.x;
+      oh[2 * k + 1] = e.y;
+      ol[2 * k] = e.z;
+      ol[2 * k + 1] = e.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t e0 = tab[idx(N0 + 2 * k)], e1 = tab[idx(N0 + 2 * k + 1)];
+      oh[k] = (e0 & 0xFFFFu) | (e1 << 16);
+      ol[k] = (e0 >> 16) | (e1 & 0xFFFF0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4_t mfma3(const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh, const u32x4_t& bl,
+                                         f32x4_t c) {
+  const f16x8_t Ah = __builtin_bit_cast(f16x8_t, ah), Al = __builtin_bit_cast(f16x8_t, al);
+  const f16x8_t Bh = __builtin_bit_cast(f16x8_t, bh), Bl = __builtin_bit_cast(f16x8_t, bl);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bl, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bh, c, 0, 0, 0);
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs a) {
+  constexpr int P = 4 / BITS;
+  constexpr int NW = D * BITS / 32;   // words per vector per stream
+  constexpr int CPL = D / 4;          // coordinates of a key per lane
+  constexpr int NWG = CPL * BITS / 32;
+  constexpr int KS = D / 32;          // k-steps of the score product
+  constexpr int CB = D / 16;          // 16-coordinate blocks of the value product
+  static_assert(NWG >= 1 && D >= 64 && D <= 128, "matrix path: d = 64 or 128, d b >= 128");
+  using G = Layout<D>;                // prologue and epilogue: the codec's lane layout
+  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
+  constexpr int VT = kMfmaKeys * D;   // halfs per plane of the value tile
+
+  __shared__ __align__(16) uint32_t tabk[256 * P];
+  __shared__ __align__(16) uint32_t tabv[256 * P];
+  __shared__ uint32_t kx[D / 2];
+  __shared__ uint32_t vsg[(D + 31) / 32];
+  __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][2 * VT];  // hi plane, lo plane
+  __shared__ __align__(16) float nrm[kWavesPerBlock][2 * kMfmaKeys];   // the iteration's key, value norms
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;  // MFMA column: query; row of the key operand: key within a block
+  const int g = lane >> 4;  // k-group: coordinates [CPL g, CPL g + CPL) of a key
+  uint16_t* vt = vtile[wv];
+  float* stage = reinterpret_cast<float*>(vt);  // [16][D] float32: queries in, results out
+
+  // unit u = (b, hkv, chunk, query group of 16), the query group fastest
+  const int64_t GQ = static_cast<int64_t>(a.group) * a.Sq;  // query vectors per key/value head
+  const int64_t NQG = (GQ + kMfmaQ - 1) / kMfmaQ;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wv;
+  const int64_t n_bh = static_cast<int64_t>(a.n_q / GQ);  // B * Hkv
+  const bool active = u < n_bh * NQG * a.n_splits;  // wave-uniform
+  const int64_t qg = u % NQG;
+  const int64_t r = u / NQG;
+  const int sp = static_cast<int>(r % a.n_splits);
+  const int64_t bh = r / a.n_splits;
+  const int64_t bb = bh / a.Hkv, hkv = bh % a.Hkv;
+  const int64_t Hq = static_cast<int64_t>(a.Hkv) * a.group;
+  const int nq = static_cast<int>(GQ - qg * kMfmaQ < kMfmaQ ? GQ - qg * kMfmaQ : kMfmaQ);
+  auto qvec = [&](int i) -> int64_t {  // query vector index of the group's i-th query
+    const int64_t qi = qg * kMfmaQ + i;
+    return (bb * Hq + hkv * a.group + qi / a.Sq) * a.Sq + qi % a.Sq;
+  };
+  // the codec's lane layout for the queries (one pass: VW >= 16 at d <= 128)
+  static_assert(VW >= kMfmaQ, "one pass over the wave's queries");
+  const int q = lane & (L - 1), vl = lane >> LOG_L;
+
+  // Positions, 32 per iteration: block k of 16 keys, lane (n, g) loads key 16 k + n's words of
+  // its coordinate slice, and lane l the norms of key l % 32 (shared through LDS); the next
+  // iteration's are loaded while the current ones are used.
+  const int64_t t0 = static_cast<int64_t>(sp) * a.chunk;
+  const int64_t t1 = t0 + a.chunk < a.S_kv ? t0 + a.chunk : a.S_kv;
+  const int64_t rowbase = bh * a.S_cap;
+  uint32_t nk1[2][NWG], nk2[2][NWG], nv1[2][NWG], nv2[2][NWG];
+  float nkn, nvn;
+  auto fetch = [&](int64_t base) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t t = base + 16 * k + n < t1 ? base + 16 * k + n : t1 - 1;
+      const int64_t row = rowbase + t;
+      load_words<NWG>(a.k1 + row * NW + g * NWG, nk1[k]);
+      load_words<NWG>(a.k2 + row * NW + g * NWG, nk2[k]);
+      load_words<NWG>(a.v1 + row * NW + g * NWG, nv1[k]);
+      load_words<NWG>(a.v2 + row * NW + g * NWG, nv2[k]);
+    }
+    const int64_t tn = base + (lane & 31) < t1 ? base + (lane & 31) : t1 - 1;
+    nkn = a.kn[rowbase + tn];
+    nvn = a.vn[rowbase + tn];
+  };
+
+  // Before the block's tables are built, start the loads: this lane's part of query vl and
+  // the first positions.
+  uint4 qraw[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) qraw[c] = make_uint4(0u, 0u, 0u, 0u);
+  if (active) {
+    if (vl < nq) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) qraw[c] = reinterpret_cast<const uint4*>(a.q + qvec(vl) * D + q * C)[c];
+    }
+    fetch(t0);
+  }
+
+  fill_mfma_table<BITS>(a.ztab_k, tabk);
+  fill_mfma_table<BITS>(a.ztab_v, tabv);
+  for (int m = threadIdx.x; m < D / 2; m += kBlockThreads) {
+    const uint32_t s0 = (a.ksign[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
+    const uint32_t s1 = (a.ksign[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
+    kx[m] = (s0 ? 0x8000u : 0u) | (s1 ? 0x80000000u : 0u);
+  }
+  for (int i = threadIdx.x; i < (D + 31) / 32; i += kBlockThreads) vsg[i] = a.vsign[i];
+  __syncthreads();
+  if (!active) return;  // no barrier follows
+
+  // 1. Rotated queries y = H diag(s_k) q (scaled by qscale) into stage[16][D].
+  {
+    const float qk = (__builtin_popcount(q) & 1) ? -a.qscale : a.qscale;
+    float y[C];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t xh[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * h];
+        const uint32_t w1 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * h + 1];
+        const float s0 = dot2_f16<0>(xh[2 * h], w0);
+        const float d0 = dot2_f16<1>(xh[2 * h], w0);
+        float* o = y + 8 * c + 4 * h;
+        o[0] = dot2_f16<0>(xh[2 * h + 1], w1, s0);
+        o[1] = dot2_f16<1>(xh[2 * h + 1], w1, d0);
+        o[2] = dot2_f16<2>(xh[2 * h + 1], w1, s0);
+        o[3] = dot2_f16<3>(xh[2 * h + 1], w1, d0);
+      }
+    }
+    lane_stages<C, 4>(y);
+    cross_stages<C, LOG_L>(y, q);
+    if (vl < kMfmaQ) {
+      float4* dst = reinterpret_cast<float4*>(stage + vl * D + q * C);
+#pragma unroll
+      for (int c = 0; c < C / 4; ++c)
+        dst[c] = make_float4(y[4 * c] * qk, y[4 * c + 1] * qk, y[4 * c + 2] * qk, y[4 * c + 3] * qk);
+    }
+  }
+  wave_lds_fence();
+
+  // 2. Query operands: lane (n, g) takes query n's coordinates [CPL g, CPL g + CPL), divided by
+  //    the query's largest magnitude qn (0 for padding queries).
+  u32x4_t qh[KS], ql[KS];
+  float qn;
+  {
+    float qv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL / 4; ++c) {
+      const float4 v = reinterpret_cast<const float4*>(stage + n * D + CPL * g)[c];
+      qv[4 * c] = v.x; qv[4 * c + 1] = v.y; qv[4 * c + 2] = v.z; qv[4 * c + 3] = v.w;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) mx = __builtin_fmaxf(mx, __builtin_fabsf(qv[j]));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    qn = mx;
+    const float inv = mx > 0.f ? 1.0f / mx : 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint2 hl = split_pair(qv[8 * s + 2 * k] * inv, qv[8 * s + 2 * k + 1] * inv);
+        qh[s][k] = hl.x;
+        ql[s][k] = hl.y;
+      }
+  }
+  wave_lds_fence();
+
+  // Softmax state of query n: reference m (base 2) of the scores and this lane's sum l of
+  // 2^(s - m); the value weights 2^(s - m) n_v are kept against their own reference mv of
+  // s + log2 n_v (so they fit fp16 whatever the norms), and the accumulator is put back on m
+  // at the end.
+  float m = -FLT_MAX, mv = -FLT_MAX, l = 0.f;
+  f32x4_t acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float* nw = nrm[wv];
+
+  for (int64_t base = t0; base < t1; base += kMfmaKeys) {
+    uint32_t k1[2][NWG], k2[2][NWG], v1[2][NWG], v2[2][NWG];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int w = 0; w < NWG; ++w) {
+        k1[k][w] = nk1[k][w]; k2[k][w] = nk2[k][w]; v1[k][w] = nv1[k][w]; v2[k][w] = nv2[k][w];
+      }
+    wave_lds_fence();
+    if (lane < 32) {
+      nw[lane] = nkn;
+      nw[kMfmaKeys + lane] = nvn;
+    }
+    wave_lds_fence();
+    float kn[2][4], vn[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float4 a4 = reinterpret_cast<const float4*>(nw + 16 * k + 4 * g)[0];
+      const float4 b4 = reinterpret_cast<const float4*>(nw + kMfmaKeys + 16 * k + 4 * g)[0];
+      kn[k][0] = a4.x; kn[k][1] = a4.y; kn[k][2] = a4.z; kn[k][3] = a4.w;
+      vn[k][0] = b4.x; vn[k][1] = b4.y; vn[k][2] = b4.z; vn[k][3] = b4.w;
+    }
+    if (base + kMfmaKeys < t1) fetch(base + kMfmaKeys);
+
+    // scores^T of the two key blocks
+    f32x4_t sc[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t lo[NWG], hi[NWG];
+      nibble_bytes<NWG>(k1[k], k2[k], lo, hi);
+      sc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      static_for<0, KS>([&](auto si) {
+        u32x4_t ah, al;
+        table_operand<BITS, NWG, decltype(si)::value>(lo, hi, tabk, ah, al);
+        sc[k] = mfma3(ah, al, qh[decltype(si)::value], ql[decltype(si)::value], sc[k]);
+      });
+    }
+
+    // online softmax of query n over the 32 keys (keys 16 k + 4 g + j in this lane)
+    float s[2][4], sv[2][4], mloc = -FLT_MAX, mvloc = -FLT_MAX;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = base + 16 * k + 4 * g + j < t1;
+        s[k][j] = valid ? sc[k][j] * qn * kn[k][j] : -FLT_MAX;
+        sv[k][j] = valid ? s[k][j] + __builtin_amdgcn_logf(vn[k][j]) : -FLT_MAX;  // v_log_f32: log2
+        mloc = __builtin_fmaxf(mloc, s[k][j]);
+        mvloc = __builtin_fmaxf(mvloc, sv[k][j]);
+      }
+    mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32));
+    mvloc = __builtin_fmaxf(mvloc, __shfl_xor(mvloc, 16));
+    mvloc = __builtin_fmaxf(mvloc, __shfl_xor(mvloc, 32));
+    if (mloc > m + kRefSlack) {
+      l *= exp2_fast(m - mloc);
+      m = mloc;
+    }
+    if (mvloc > mv + kRefSlack) {
+      const float f = exp2_fast(mv - mvloc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] *= f;
+      mv = mvloc;
+    }
+    u32x4_t ph, pl;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float pw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l += exp2_fast(s[k][j] - m);
+        pw[j] = exp2_fast(sv[k][j] - mv);
+      }
+      const uint2 h0 = split_pair(pw[0], pw[1]), h1 = split_pair(pw[2], pw[3]);
+      ph[2 * k] = h0.x;
+      pl[2 * k] = h0.y;
+      ph[2 * k + 1] = h1.x;
+      pl[2 * k + 1] = h1.y;
+    }
+
+    // values of the 32 keys into the tile (row = key, 8-half chunks swizzled by row & 7)
+    wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t lo[NWG], hi[NWG];
+      nibble_bytes<NWG>(v1[k], v2[k], lo, hi);
+      const int row = 16 * k + n;
+      static_for<0, KS>([&](auto si) {
+        constexpr int S = decltype(si)::value;
+        u32x4_t vh, vlo;
+        table_operand<BITS, NWG, S>(lo, hi, tabv, vh, vlo);
+        const int ch = ((CPL * g + 8 * S) >> 3) ^ (row & 7);
+        *reinterpret_cast<u32x4_t*>(vt + row * D + 8 * ch) = vh;
+        *reinterpret_cast<u32x4_t*>(vt + VT + row * D + 8 * ch) = vlo;
+      });
+    }
+    wave_lds_fence();
+
+    // out^T += Z_v^T P^T: lane (n, g) reads coordinate 16 cb + n of keys 4 g + [0, 4) and
+    // 16 + 4 g + [0, 4) (its k-slots 8 g + [0, 8)), transposed out of the tile
+    {
+      const int jr = n >> 2, jc = n & 3;  // this lane addresses row kb + jr, coordinates 4 jc..
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        u32x4_t vh, vlo;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int row = 16 * hlf + 4 * g + jr;
+          const int ch = (2 * cb + (jc >> 1)) ^ (row & 7);
+          const int off = row * D + 8 * ch + 4 * (jc & 1);
+          typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+          const i16x4_t th = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)((__attribute__((address_space(3))) uint16_t*)(vt + off)));
+          const i16x4_t tl = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)((__attribute__((address_space(3))) uint16_t*)(vt + VT + off)));
+          const u32x2_t uh = __builtin_bit_cast(u32x2_t, th), ul = __builtin_bit_cast(u32x2_t, tl);
+          vh[2 * hlf] = uh[0]; vh[2 * hlf + 1] = uh[1];
+          vlo[2 * hlf] = ul[0]; vlo[2 * hlf + 1] = ul[1];
+        }
+        acc[cb] = mfma3(vh, vlo, ph, pl, acc[cb]);
+      }
+    }
+  }
+
+  // 5. The query's sum over the four lane groups, its accumulator (coordinates 16 cb + 4 g +
+  //    [0, 4) of query n) through LDS into the codec's layout, rotated back, written.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  wave_lds_fence();
+  const float back = exp2_fast(mv - m);  // accumulator from reference mv onto m
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+    reinterpret_cast<float4*>(stage + n * D + 16 * cb + 4 * g)[0] =
+        make_float4(acc[cb][0] * back, acc[cb][1] * back, acc[cb][2] * back, acc[cb][3] * back);
+  wave_lds_fence();
+  if (g == 0 && n < nq) {
+    float* ws = a.ws + (qvec(n) * a.n_splits + sp) * (D + 4);
+    ws[0] = m;
+    ws[1] = l;
+  }
+  {
+    const int q = lane & (L - 1), vl = lane >> LOG_L;
+#pragma unroll
+    for (int p0 = 0; p0 < kMfmaQ; p0 += VW) {
+      const int i = p0 + vl;
+      float z[C];
+#pragma unroll
+      for (int c = 0; c < C / 4; ++c) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < kMfmaQ) v = reinterpret_cast<const float4*>(stage + i * D + q * C)[c];
+        z[4 * c] = v.x; z[4 * c + 1] = v.y; z[4 * c + 2] = v.z; z[4 * c + 3] = v.w;
+      }
+      unrotate_f32<D, 32>(z, q, a.inv_sqrt_d, vsg);
+      if (i < nq) {
+        float4* wa = reinterpret_cast<float4*>(a.ws + (qvec(i) * a.n_splits + sp) * (D + 4) + 4 + q * C);
+#pragma unroll
+        for (int c = 0; c < C / 4; ++c) wa[c] = make_float4(z[4 * c], z[4 * c + 1], z[4 * c + 2], z[4 * c + 3]);
+      }
+    }
+  }
+}
+
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplits = 4096;  // chunks per query vector (the host plan keeps below this)
 
@@ -409,8 +854,27 @@ static hipError_t launch_attend_t(const AttendArgs& a, hipStream_t stream) {
                          stream);
 }
 
+// The matrix-core partial pass (16 query vectors per wave unit), then the combine.
+template <int D, int BITS>
+static hipError_t launch_attend_mfma_t(const AttendArgs& a, hipStream_t stream) {
+  void* args[] = {const_cast<AttendArgs*>(&a)};
+  const int64_t gq = static_cast<int64_t>(a.group) * a.Sq;
+  const int64_t units = (a.n_q / gq) * ((gq + kMfmaQ - 1) / kMfmaQ) * a.n_splits;
+  const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > INT_MAX || a.n_q * (D / combine_slice<D>()) > INT_MAX) return hipErrorInvalidValue;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attend_mfma<D, BITS>),
+                                 dim3(static_cast<int>(blocks)), dim3(kBlockThreads), args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_combine<D>),
+                         dim3(static_cast<int>(a.n_q * (D / combine_slice<D>()))), dim3(kCombineThreads), args, 0,
+                         stream);
+}
+
 template <int D, int BITS>
 static auto attend_nqw(int nqw) -> hipError_t (*)(const AttendArgs&, hipStream_t) {
+  if constexpr ((D == 64 || D == 128) && BITS != 3 && D * BITS >= 128) {
+    if (nqw == kMfmaQ) return launch_attend_mfma_t<D, BITS>;
+  }
   if (nqw == 1) return launch_attend_t<D, BITS, 1>;
   if constexpr (D <= 512) {
     if (nqw == 2) return launch_attend_t<D, BITS, 2>;
@@ -431,7 +895,8 @@ static auto attend_fn(int bits, int nqw) -> hipError_t (*)(const AttendArgs&, hi
 }
 
 // Launcher used by api.cpp: both kernels on `stream`, the combine after the partials.
-// nqw: query vectors per wave (1, 2 or 4; a divisor of group * Sq; 1 for d = 1024).
+// nqw: query vectors per wave: 16 selects the matrix-core pass (d = 64 or 128, b = 1, 2 or
+// 4, d b >= 128); else 1, 2 or 4 (a divisor of group * Sq; 1 for d = 1024).
 hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream) {
   hipError_t (*f)(const AttendArgs&, hipStream_t) = nullptr;
   switch (d) {

@@ -34,6 +34,21 @@ struct Layout {
 
 // ------------------------------------------------------------------------------ helpers
 
+// Compile-time integer, and a loop over [I, N) whose body sees the index as one (so code
+// that indexes register arrays with it stays fully unrolled).
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+
 // LDS chunk swizzle for a wave buffer of 64 rows (one per lane) x CH 16-byte chunks. Any
 // 16 consecutive lanes then touch 16 distinct 16-byte bank groups, both when a lane writes
 // chunk (64k + lane) of the tile and when lane r reads chunk c of its own row r.

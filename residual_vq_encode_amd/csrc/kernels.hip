@@ -40,20 +40,6 @@
 
 namespace kvq {
 
-// Compile-time integer, and a loop over [I, N) whose body sees the index as one (so code
-// that indexes register arrays with it stays fully unrolled).
-template <int V>
-struct Int {
-  static constexpr int value = V;
-};
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Int<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // Residency targets (waves per SIMD); the register allocator is held to 512 / target VGPRs.
 constexpr int kEncodeWavesPerEU = 4;
 constexpr int kDecodeWavesPerEU = 4;

@@ -174,33 +174,45 @@ def test_attend_host_side_argument_checks():
     assert att(ptrs=(A, A, None, A, A, A)) == -1
     assert att(q=A + 2) == -3 and att(out=A + 8) == -3 and att(ws=A + 4) == -3
     assert att(ptrs=(A + 4, A, A, A, A, A)) == -3 and att(ptrs=(A, A, A + 2, A, A, A)) == -3
-    need = kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 50)
+    need = kvq.kvq_rvq_attend_workspace_size(128, 2, 1, 4, 1, 2, 50)
     assert need > 0 and att(wsb=need - 1) == -4
-    assert lib.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 50, None) == -1
+    assert lib.kvq_rvq_attend_workspace_size(128, 2, 1, 4, 1, 2, 50, None) == -1
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_rvq_attend_workspace_size(96, 1, 4, 1, 2, 50)
+        kvq.kvq_rvq_attend_workspace_size(96, 2, 1, 4, 1, 2, 50)
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 2, 0)
+        kvq.kvq_rvq_attend_workspace_size(128, 2, 1, 4, 1, 2, 0)
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_rvq_attend_workspace_size(128, 1, 4, 1, 3, 50)
-    # plan: nqw query vectors per wave (4, 2 or 1, dividing the query vectors per key/value
-    # head); chunks of whole wave iterations (64 / (d / 16) positions with nqw > 1, else
-    # 64 / (d / 32)), about 2048 waves, at least 8 iterations each
-    for (d, B, Hq, Sq, Hkv, S_kv, nqw) in ((128, 1, 32, 1, 8, 32768, 4), (128, 1, 1, 1, 1, 5, 1),
-                                           (128, 4, 8, 3, 4, 1000, 2), (128, 1, 32, 1, 32, 1, 1),
-                                           (64, 2, 6, 1, 2, 700, 1), (1024, 1, 8, 1, 2, 3000, 1),
-                                           (16, 1, 4, 2, 1, 77, 4), (128, 1, 1, 1, 1, 10 ** 7, 1)):
+        kvq.kvq_rvq_attend_workspace_size(128, 2, 1, 4, 1, 3, 50)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_rvq_attend_workspace_size(128, 5, 1, 4, 1, 2, 50)
+    # plan. Matrix path (d = 64 or 128, b = 1, 2, 4, d b >= 128): 16 query vectors per wave
+    # unit, units per split = heads x ceil(queries per head / 16), chunks of 32-position
+    # iterations, at least 4. Otherwise nqw query vectors per wave (4, 2 or 1, dividing the
+    # query vectors per head), chunks of 64 / (d / 16) positions with nqw > 1, else
+    # 64 / (d / 32), at least 8 iterations. Both: about 2048 waves, at most 4096 chunks.
+    for (d, bits, B, Hq, Sq, Hkv, S_kv) in ((128, 2, 1, 32, 1, 8, 32768), (128, 2, 1, 1, 1, 1, 5),
+                                            (128, 3, 4, 8, 3, 4, 1000), (128, 3, 1, 32, 1, 32, 1),
+                                            (64, 1, 2, 6, 1, 2, 700), (64, 2, 2, 6, 1, 2, 700),
+                                            (1024, 2, 1, 8, 1, 2, 3000), (16, 4, 1, 4, 2, 1, 77),
+                                            (128, 4, 1, 1, 1, 1, 10 ** 7), (128, 3, 1, 1, 1, 1, 10 ** 7),
+                                            (128, 1, 2, 40, 1, 2, 5000)):
         nq = B * Hq * Sq
-        cm = 16 if nqw > 1 and d >= 32 else 32
-        vw = 64 // (d // min(d, cm))
-        splits0 = -(-2048 * nqw // nq)
+        gq = (Hq // Hkv) * Sq
+        if d in (64, 128) and bits != 3 and d * bits >= 128:
+            vw, min_it, per_split = 32, 4, (nq // gq) * -(-gq // 16)
+        else:
+            nqw = (4 if gq % 4 == 0 else 2 if gq % 2 == 0 else 1) if d <= 512 else 1
+            cm = 16 if nqw > 1 and d >= 32 else 32
+            vw, min_it, per_split = 64 // (d // min(d, cm)), 8, nq // nqw
+        splits0 = -(-2048 // per_split)
         chunk = -(-S_kv // splits0)
-        chunk = max(-(-chunk // vw) * vw, 8 * vw)
+        chunk = max(-(-chunk // vw) * vw, min_it * vw)
         min_chunk = -(-S_kv // 4096)
         if chunk < min_chunk:
             chunk = -(-min_chunk // vw) * vw
         n_splits = -(-S_kv // chunk)
-        assert kvq.kvq_rvq_attend_workspace_size(d, B, Hq, Sq, Hkv, S_kv) == nq * n_splits * (d + 4) * 4
+        assert kvq.kvq_rvq_attend_workspace_size(d, bits, B, Hq, Sq, Hkv, S_kv) == nq * n_splits * (d + 4) * 4, \
+            (d, bits, B, Hq, Sq, Hkv, S_kv)
 
 
 def test_python_binding_rejects_cpu_tensors():
