@@ -8,11 +8,12 @@ signs), then the unpack+decode of the packed result. Inputs are resident in HBM 
 timing starts and rotate through a pool of distinct tensors (and distinct output buffers)
 larger than twice the 256 MB last-level cache, so every encode streams its input from HBM.
 
-Timing: the K steps run as K encode launches back to back on one stream, then the K
-matching decode launches; HIP events recorded on that stream bracket each group, and the
-timed region is bracketed by device synchronisation on both sides. The average encode
-launch duration is the encode group's span over K (it includes the gaps between
-back-to-back launches). `value` is encode+pack throughput: algorithmic bytes per launch
+Timing: the K steps run in blocks of 10 on one stream: 10 encode launches back to back,
+then the 10 matching decode launches, then the next block. HIP events recorded on that
+stream bracket every block, and the timed region is bracketed by device synchronisation on
+both sides. The average encode launch duration is the sum of the encode blocks' spans over
+K (it includes the gaps between back-to-back launches); the per-block averages give p10,
+p50, p90 and an A/A noise floor (even against odd blocks). `value` is encode+pack throughput: algorithmic bytes per launch
 (fp16 bytes in + packed bytes out; the 4-byte norms are reported separately, not counted)
 over that average, checked against the 8 TB/s HBM peak in `roofline`. `cpu_baseline` is
 the CPU oracle timed on a bounded sample of the same tensor.
@@ -63,6 +64,24 @@ SIGN_WORKLOADS = {"rabitq_llama_layer": ("llama_layer", "rabitq", 0, 8),
 # key/value heads of the gqa_long cache shape [1, 8, 32768, 128], b = 2, keys and values)
 ATTEND_WORKLOADS = {"attend_decode": {"B": 1, "Hq": 32, "Hkv": 8, "Sq": 1, "S_kv": 32768, "D": 128, "bits": 2,
                                       "pool": 16}}
+
+
+BLOCK = 10  # launches per timed block
+
+
+def spread(per_block):
+    """p10 / p50 / p90 of per-launch block averages (us), and the A/A noise floor: the
+    relative gap between the medians of the even and the odd blocks (the same kernel on the
+    same pool, interleaved in time)."""
+    import numpy as np
+    v = np.asarray(per_block, dtype=np.float64)
+    out = {"blocks": int(v.size), "launches_per_block": BLOCK}
+    for q in (10, 50, 90):
+        out[f"p{q}"] = round(float(np.percentile(v, q)), 3)
+    if v.size >= 4:
+        a, b = float(np.median(v[0::2])), float(np.median(v[1::2]))
+        out["aa_noise"] = round(abs(a - b) / float(np.median(v)), 4)
+    return out
 
 
 def kernel_source_hash() -> str:
@@ -146,10 +165,12 @@ def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int)
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; decode_append: its 2000 steps)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama_layer",
-                    choices=sorted(WORKLOADS) + sorted(ATTEND_WORKLOADS) + sorted(SIGN_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(ATTEND_WORKLOADS) + sorted(SIGN_WORKLOADS)
+                    + ["decode_append"])
     ap.add_argument("--pool", type=int, default=None, help="distinct input tensors to rotate through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -180,6 +201,10 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.workload == "decode_append":
+        return bench_append(args)
+    if args.steps is None:
+        args.steps = 200
     if args.workload in ATTEND_WORKLOADS:
         return bench_attend(args)
     if args.workload in SIGN_WORKLOADS:
@@ -230,23 +255,30 @@ def main() -> int:
         dec(i % P)
     torch.cuda.synchronize()
 
+    # The K steps run in blocks: a block of encodes back to back, then the same tensors'
+    # decodes, the two kernels taking turns. Events between the blocks give per-block
+    # averages (their spread, and an A/A noise floor from alternate encode blocks).
     K = args.steps
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    blocks = [(a, min(a + BLOCK, K)) for a in range(0, K, BLOCK)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(blocks) + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        enc((args.warmup + i) % P)
-    e1.record(stream)
-    for i in range(K):
-        dec((args.warmup + i) % P)
-    e2.record(stream)
+    ev[0].record(stream)
+    for bi, (a, b) in enumerate(blocks):
+        for i in range(a, b):
+            enc((args.warmup + i) % P)
+        ev[2 * bi + 1].record(stream)
+        for i in range(a, b):
+            dec((args.warmup + i) % P)
+        ev[2 * bi + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    enc_us = e0.elapsed_time(e1) * 1e3 / K
-    dec_us = e1.elapsed_time(e2) * 1e3 / K
-    total_ms = e0.elapsed_time(e2)
+    enc_blk = [ev[2 * bi].elapsed_time(ev[2 * bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+    dec_blk = [ev[2 * bi + 1].elapsed_time(ev[2 * bi + 2]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+    enc_us = sum(t * (b - a) for t, (a, b) in zip(enc_blk, blocks)) / K
+    dec_us = sum(t * (b - a) for t, (a, b) in zip(dec_blk, blocks)) / K
+    total_ms = ev[0].elapsed_time(ev[-1])
     n_vec = B * H * S
     enc_bytes = n_vec * (D * 2 + stages * nw * 4)
     dec_bytes = n_vec * (stages * nw * 4 + 4 + D * 2)
@@ -294,7 +326,9 @@ def main() -> int:
         "tokens_per_s": round(B * S / (enc_us * 1e-6), 1),
         "head_vectors_per_s": round(n_vec / (enc_us * 1e-6), 1),
         "encode_us_per_launch": round(enc_us, 3),
+        "encode_us_blocks": spread(enc_blk),
         "decode_us_per_launch": round(dec_us, 3),
+        "decode_us_blocks": spread(dec_blk),
         "decode_GBps": round(dec_gbps, 1),
         "norm_bytes_per_launch_not_counted": n_vec * 4,
         "wall_s_timed_region": round(wall, 4),
@@ -522,6 +556,130 @@ def bench_attend(args) -> int:
                          "sample": f"the whole step ({B * Hq * Sq} query vectors over {S} positions), "
                                    f"{dt_oracle:.1f} s wall, numpy float64 oracle"},
     }
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
+def bench_append(args) -> int:
+    """Decode-step appends: step t encodes one token for every (batch, head) of
+    [256, 8, 1, 128] into caches [256, 8, 32768, n_words] at s_offset = t. K steps with
+    distinct inputs run back to back twice: launched one by one from the host (eager), and
+    replayed from one captured graph of the same K launches. The graph's span is the device
+    time per step; the eager span also counts the host's launch cost."""
+    import numpy as np
+    import torch
+
+    import residual_vq_encode_amd as kvq
+    import synth
+    from oracle import codebooks as ocb
+    from oracle import flips, rvq
+
+    w = synth.WORKLOADS["decode_append"]
+    spec = w.tensors[0]
+    B, H, D, S_cap = spec.B, spec.H, spec.D, synth.DECODE_APPEND_S_CAP
+    bits = w.bits[0]
+    K = min(args.steps if args.steps is not None else spec.S, spec.S)
+    dev = torch.device("cuda:0")
+    signs = synth.signs(w.sign_seed, D).numpy()
+    cb = kvq.build_codebooks(D, bits, signs)
+    nw = cb.n_words
+    p1 = torch.empty((B, H, S_cap, nw), dtype=torch.int32, device=dev)
+    p2 = torch.empty_like(p1)
+    nrm = torch.empty((B, H, S_cap), dtype=torch.float32, device=dev)
+    steps = [synth.step_rows(spec, t, device=dev).contiguous() for t in range(K)]
+    stream = torch.cuda.current_stream()
+
+    def run_all():
+        st = torch.cuda.current_stream()
+        for t in range(K):
+            kvq.kvq_rvq_encode_pack(cb, steps[t], p1, p2, nrm, t, st)
+
+    for t in range(min(args.warmup, K)):
+        kvq.kvq_rvq_encode_pack(cb, steps[t], p1, p2, nrm, t, stream)
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    run_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - wall0
+    eager_us = e0.elapsed_time(e1) * 1e3 / K
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run_all()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()  # untimed first replay
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    g0.record(stream)
+    g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    graph_us = g0.elapsed_time(g1) * 1e3 / K
+
+    # parity of sampled steps of the replayed caches against the oracle
+    t_tab = ocb.build_tables(D, bits)
+    ok = True
+    n_flip = n_codes = 0
+    for t in sorted({0, K // 2, K - 1}):
+        rows = steps[t].reshape(-1, D).cpu().numpy()
+        ref = rvq.encode(rows, signs, t_tab)
+        rep = flips.compare_encode(p1[:, :, t].reshape(-1, nw).cpu().numpy().view(np.uint32),
+                                   p2[:, :, t].reshape(-1, nw).cpu().numpy().view(np.uint32),
+                                   nrm[:, :, t].reshape(-1).cpu().numpy(), ref, t_tab, 1e-5)
+        ok = ok and rep.ok(max(1e-6, 1.0 / max(1, rep.n_codes)), 1e-6)
+        n_flip += rep.flip_fraction * rep.n_codes
+        n_codes += rep.n_codes
+
+    step_bytes = B * H * (D * 2 + 2 * nw * 4)
+    result = {
+        "metric": "decode-step append: tokens/s (one token of every sequence per step) and us/step",
+        "value": round(B / (graph_us * 1e-6), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(graph_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator; no dataset)",
+        "config": {"workload": f"decode_append: {K} steps of [{B},{H},1,{D}] appended into S_cap={S_cap} caches; b={bits}",
+                   "bits": bits, "timing": "one captured graph of the K launches, replayed"},
+        "us_per_step_graph": round(graph_us, 3),
+        "us_per_step_eager": round(eager_us, 3),
+        "wall_s_timed_region": round(wall, 4),
+        "wall_s_eager": round(wall_eager, 4),
+        "parity_recheck": {"steps": sorted({0, K // 2, K - 1}), "flip_fraction": n_flip / max(1, n_codes), "ok": bool(ok)},
+        "roofline": {"bound": "launch", "achieved": round(step_bytes / (graph_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(step_bytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 5),
+                     "traffic": None, "algorithmic_bytes_per_launch": step_bytes,
+                     "kernel": f"kvq::encode_kernel<{D}, {bits}, false, 2>"},
+    }
+    if not args.no_cpu_baseline:
+        n_s = min(K, 20)
+        x = np.concatenate([steps[t].reshape(-1, D).cpu().numpy() for t in range(n_s)])
+        t0 = time.perf_counter()
+        rvq.encode(x, signs, t_tab)
+        dt = time.perf_counter() - t0
+        try:
+            import threadpoolctl
+            cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+        except Exception:
+            cores = os.cpu_count()
+        result["cpu_baseline"] = {"value": round(n_s * B / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                                  "sample": f"the first {n_s} steps ({n_s * B * H} vectors), encode+pack, {dt:.2f} s wall, "
+                                            f"numpy float64 oracle"}
     print(json.dumps(result), flush=True)
     return 0 if ok else 1
 
