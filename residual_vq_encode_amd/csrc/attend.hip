@@ -445,12 +445,25 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
   constexpr int VT = kMfmaKeys * D;   // halfs per plane of the value tile
 
-  __shared__ __align__(16) uint32_t tabk[256 * P];
-  __shared__ __align__(16) uint32_t tabv[256 * P];
-  __shared__ uint32_t kx[D / 2];
-  __shared__ uint32_t vsg[(D + 31) / 32];
-  __shared__ __align__(16) uint16_t vtile[kWavesPerBlock][2 * VT];  // hi plane, lo plane
-  __shared__ __align__(16) float nrm[kWavesPerBlock][2 * kMfmaKeys];   // the iteration's key, value norms
+  // The block's LDS in one struct, small tables first: every table address is then a lane
+  // offset plus an immediate below 64 KiB, which the LDS instructions encode themselves (as
+  // separate variables the tables landed above the 64 KiB value tile, and each lookup paid
+  // for an address add).
+  struct Smem {
+    alignas(16) uint32_t tabk[256 * P];
+    alignas(16) uint32_t tabv[256 * P];
+    alignas(16) uint32_t kx[D / 2];
+    alignas(16) uint32_t vsg[(D + 31) / 32];
+    alignas(16) float nrm[kWavesPerBlock][2 * kMfmaKeys];  // the iteration's key, value norms
+    alignas(16) uint16_t vtile[kWavesPerBlock][2 * VT];    // hi plane, lo plane
+  };
+  __shared__ Smem sm;
+  auto& tabk = sm.tabk;
+  auto& tabv = sm.tabv;
+  auto& kx = sm.kx;
+  auto& vsg = sm.vsg;
+  auto& nrm = sm.nrm;
+  auto& vtile = sm.vtile;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // MFMA column: query; row of the key operand: key within a block
