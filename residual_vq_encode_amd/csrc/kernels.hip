@@ -44,6 +44,15 @@ namespace kvq {
 constexpr int kEncodeWavesPerEU = 4;
 constexpr int kDecodeWavesPerEU = 4;
 
+// The cache-window encodes (general row mapping) at 3 and 4 bits need about 165-180
+// registers: held to 128 they spilled 150-250 bytes per lane and ran 1.5-3x slower than the
+// contiguous encode (b = 4 window 95 us against 30 us on [1,8,32768,128]); at 3 waves per
+// SIMD they run at 35 and 39 us.
+template <int BITS, bool CONTIG>
+constexpr int encode_waves_per_eu() {
+  return (!CONTIG && BITS >= 3) ? 3 : kEncodeWavesPerEU;
+}
+
 // ------------------------------------------------------------------------------ encode
 
 // STAGES = 2: the two-stage residual codec (both code streams); STAGES = 1: the single-stage
@@ -52,7 +61,7 @@ constexpr int kDecodeWavesPerEU = 4;
 // the rotated vector with its norm ("rvq" tag page, "A fusion this codebase had already
 // proven out": rotate, binarize, pack and magnitude in one kernel), stream 1 only.
 template <int D, int BITS, bool CONTIG, int STAGES>
-__global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_kernel(const EncodeArgs a) {
+__global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>())) void encode_kernel(const EncodeArgs a) {
   using G = Layout<D>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
   constexpr int EPW = 32 / BITS;                     // codes per word
