@@ -15,7 +15,6 @@ hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipSt
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream);
 hipError_t launch_qjl(const QjlArgs& a, int d, int m, hipStream_t stream);
-int64_t qjl_lds_need(int d, int m);
 }  // namespace kvq
 
 namespace {
@@ -264,7 +263,7 @@ extern "C" kvq_status kvq_rabitq_encode_pack(const kvq_codebooks* cb, const uint
 extern "C" kvq_status kvq_qjl_supported(int32_t d, int32_t m) {
   if (d != 32 && d != 64 && d != 128 && d != 256) return KVQ_ERR_SHAPE;
   if (m < 32 || m > 256 || m % 32 != 0) return KVQ_ERR_SHAPE;
-  if (kvq::qjl_lds_need(d, m) > 160 * 1024) return KVQ_ERR_SHAPE;
+  if (kvq::qjl_lds_need(d, m) > kvq::kQjlLdsMax) return KVQ_ERR_SHAPE;
   return KVQ_OK;
 }
 

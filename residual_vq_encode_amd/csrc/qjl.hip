@@ -31,21 +31,6 @@ namespace kvq {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kQjlTile = 32;  // keys per wave tile: the 32 columns of one MFMA block
-
-// Waves per block: each holds a tile of 32 keys (64 d bytes) in LDS next to the one copy
-// of the sketch the block shares. At d = 128, m = 128 a block takes 64 KiB, so two blocks
-// (two waves per SIMD) share a CU. Measured on the Llama-layer keys: 4 waves per block
-// 19.0 us, 8 waves 20.9 us, 16 waves (one block per CU) 19.7 us; the sketch held in
-// registers instead of LDS 20.6 us. The loads alone take 15.4 us and the arithmetic alone
-// 11-13 us, so the remaining loss is their imperfect overlap.
-template <int D>
-constexpr int qjl_waves() {
-  return 4;
-}
-
-constexpr int64_t kQjlLdsMax = 160 * 1024;  // LDS per workgroup (and per CU) on gfx950
-
 // LDS chunk swizzle: chunk c of row r (a sketch row or a key of the tile) is stored at
 // position c ^ (r & mask), so the 32 rows an MFMA operand read touches spread over the
 // banks instead of all hitting one 16-byte group.
@@ -54,11 +39,6 @@ constexpr int qjl_chunk_mask() {
   return (D / 8 < 16 ? D / 8 : 16) - 1;
 }
 
-// LDS bytes of one block: the sketch (m rows of d fp16) and one tile per wave.
-template <int D>
-constexpr int64_t qjl_lds_bytes(int m) {
-  return (static_cast<int64_t>(m) * D + static_cast<int64_t>(qjl_waves<D>()) * kQjlTile * D) * 2;
-}
 
 template <int D, int MB, bool CONTIG>
 __global__ __launch_bounds__(qjl_waves<D>() * 64) void qjl_encode_kernel(const QjlArgs a) {
@@ -238,17 +218,6 @@ static hipError_t launch_qjl_d(const QjlArgs& a, int m, hipStream_t stream) {
     default: break;
   }
   return hipErrorInvalidValue;
-}
-
-// LDS bytes a launch needs for head dimension d and sketch size m (0: unsupported d).
-int64_t qjl_lds_need(int d, int m) {
-  switch (d) {
-    case 32: return qjl_lds_bytes<32>(m);
-    case 64: return qjl_lds_bytes<64>(m);
-    case 128: return qjl_lds_bytes<128>(m);
-    case 256: return qjl_lds_bytes<256>(m);
-    default: return 0;
-  }
 }
 
 // Launcher used by api.cpp.

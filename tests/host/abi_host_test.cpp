@@ -1,0 +1,251 @@
+// Host-only test of libkvq's C ABI, built with AddressSanitizer and UBSan against the launch
+// stubs of launch_stubs.cpp (no GPU, nothing launched): codebook construction for every
+// supported (d, bits), every argument check of every entry point, the argument blocks the
+// checks hand to the launchers, and the attention plan. Device pointers are fake, aligned
+// addresses; the stubs never dereference them. Prints "ok" and exits 0 when every check
+// holds.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kvq.h"
+#include "launch_stubs.h"
+
+namespace {
+
+int g_fail = 0;
+
+#define CHECK(cond)                                                  \
+  do {                                                               \
+    if (!(cond)) {                                                   \
+      std::fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++g_fail;                                                      \
+    }                                                                \
+  } while (0)
+
+template <typename T>
+T* fake(uintptr_t addr) {
+  return reinterpret_cast<T*>(addr);
+}
+
+// ------------------------------------------------------------------------------ codebooks
+
+void test_codebooks() {
+  kvq_codebooks cb;
+  for (int d = 8; d <= 1024; d *= 2) {
+    std::vector<int8_t> neg(d, -1);
+    for (int bits = 1; bits <= 4; ++bits) {
+      CHECK(kvq_build_codebooks(d, bits, nullptr, &cb) == KVQ_OK);
+      const int L = 1 << bits, epw = 32 / bits;
+      CHECK(cb.d == d && cb.bits == bits && cb.elems_per_word == epw);
+      CHECK(cb.n_words == (d + epw - 1) / epw);
+      for (int k = 0; k < L; ++k) {
+        CHECK(cb.c1[k] == -cb.c1[L - 1 - k]);  // exactly antisymmetric
+        CHECK(cb.c2[k] == -cb.c2[L - 1 - k]);
+      }
+      for (int k = 0; k + 1 < L; ++k) {
+        CHECK(cb.c1[k] < cb.c1[k + 1] && cb.c2[k] < cb.c2[k + 1]);
+        CHECK(cb.c1[k] < cb.b1[k] && cb.b1[k] < cb.c1[k + 1]);
+        CHECK(cb.c2[k] < cb.b2[k] && cb.b2[k] < cb.c2[k + 1]);
+      }
+      uint32_t mid;  // the middle boundary is +0 (sign bit clear)
+      std::memcpy(&mid, &cb.b1[L / 2 - 1], 4);
+      CHECK(mid == 0u);
+      std::memcpy(&mid, &cb.b2[L / 2 - 1], 4);
+      CHECK(mid == 0u);
+      CHECK(std::fabs(cb.sigma1 - 1.0 / std::sqrt(static_cast<double>(d))) < 1e-15);
+      for (int w = 0; w < KVQ_MAX_D / 32; ++w) CHECK(cb.sign_bits[w] == 0u);
+      CHECK(kvq_build_codebooks(d, bits, neg.data(), &cb) == KVQ_OK);
+      for (int j = 0; j < KVQ_MAX_D; ++j) CHECK(((cb.sign_bits[j >> 5] >> (j & 31)) & 1u) == (j < d ? 1u : 0u));
+    }
+    neg[d - 1] = 0;  // not a sign
+    CHECK(kvq_build_codebooks(d, 2, neg.data(), &cb) == KVQ_ERR_ARG);
+  }
+  CHECK(kvq_build_codebooks(128, 2, nullptr, nullptr) == KVQ_ERR_ARG);
+  for (int d : {0, 4, 7, 12, 96, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
+  for (int bits : {0, 5, -1}) CHECK(kvq_build_codebooks(128, bits, nullptr, &cb) == KVQ_ERR_SHAPE);
+}
+
+// ------------------------------------------------------------------------ encode / decode
+
+void test_encode_decode() {
+  kvq_codebooks cb;
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &cb) == KVQ_OK);
+  uint16_t* x = fake<uint16_t>(0x10000);
+  uint32_t* p1 = fake<uint32_t>(0x20000);
+  uint32_t* p2 = fake<uint32_t>(0x30000);
+  float* nr = fake<float>(0x40000);
+  kvq::g_stub = kvq::StubLog{};
+
+  // contiguous cache: row map is the identity
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.encode_calls == 1 && kvq::g_stub.enc.n_vec == 30 && kvq::g_stub.enc.map.contiguous == 1);
+  CHECK(kvq::g_stub.d == 128 && kvq::g_stub.bits == 2 && kvq::g_stub.stages == 2);
+  CHECK(kvq::g_stub.enc.x == x && kvq::g_stub.enc.p1 == p1 && kvq::g_stub.enc.p2 == p2 && kvq::g_stub.enc.norms == nr);
+  // a window of a larger cache
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 100, 7, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.enc.map.contiguous == 0 && kvq::g_stub.enc.map.S == 5 && kvq::g_stub.enc.map.S_cap == 100 &&
+        kvq::g_stub.enc.map.s_offset == 7);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 100, 95, nullptr) == KVQ_OK);  // ends at S_cap
+  // range, shape, alignment, null checks
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 100, 96, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 4, 0, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 100, -1, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_encode_pack(&cb, x, -1, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_SHAPE);
+  CHECK(kvq_rvq_encode_pack(&cb, x, int64_t(1) << 40, int64_t(1) << 40, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_encode_pack(&cb, fake<uint16_t>(0x10002), 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, fake<uint32_t>(0x20004), p2, nr, 5, 0, nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, fake<float>(0x40002), 5, 0, nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq_rvq_encode_pack(&cb, nullptr, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, nullptr, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
+  CHECK(kvq_rvq_encode_pack(nullptr, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
+  kvq_codebooks bad = cb;
+  bad.n_words = 9;
+  CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
+  bad = cb;
+  bad.d = 96;
+  CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_SHAPE);
+  const int before = kvq::g_stub.encode_calls;
+  CHECK(kvq_rvq_encode_pack(&cb, nullptr, 0, 3, 5, nullptr, nullptr, nullptr, 5, 0, nullptr) == KVQ_OK);  // empty
+  CHECK(kvq::g_stub.encode_calls == before);
+
+  // single-stage codec and the sign code go through the same launcher with fewer stages
+  CHECK(kvq_mse_encode_pack(&cb, x, 1, 1, 8, p1, nr, 8, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.stages == 1 && kvq::g_stub.enc.p2 == nullptr);
+  kvq_codebooks cb1;
+  CHECK(kvq_build_codebooks(128, 1, nullptr, &cb1) == KVQ_OK);
+  CHECK(kvq_rabitq_encode_pack(&cb1, x, 1, 1, 8, p1, nr, 8, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.stages == 0 && kvq::g_stub.bits == 1);
+  CHECK(kvq_rabitq_encode_pack(&cb, x, 1, 1, 8, p1, nr, 8, 0, nullptr) == KVQ_ERR_SHAPE);  // 2-bit codebooks
+
+  // decode
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 2, 3, 100, 7, 5, x, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.decode_calls == 1 && kvq::g_stub.dec.n_vec == 30 && kvq::g_stub.dec.map.s_offset == 7);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nullptr, 2, 3, 5, 0, 5, x, nullptr) == KVQ_OK);  // unit mode
+  CHECK(kvq::g_stub.dec.norms == nullptr && kvq::g_stub.dec.map.contiguous == 1);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 2, 3, 100, 96, 5, x, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, nullptr, nr, 2, 3, 5, 0, 5, x, nullptr) == KVQ_ERR_ARG);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 2, 3, 5, 0, 5, fake<uint16_t>(0x10008), nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq_mse_unpack_decode(&cb, p1, nr, 1, 1, 8, 0, 8, x, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.stages == 1);
+}
+
+// ------------------------------------------------------------------------------ QJL
+
+void test_qjl() {
+  for (int d : {32, 64, 128, 256})
+    for (int m = 32; m <= 256; m += 32) {
+      const bool fits = (static_cast<int64_t>(m) * d + 4 * 32 * d) * 2 <= 160 * 1024;
+      CHECK(kvq_qjl_supported(d, m) == (fits ? KVQ_OK : KVQ_ERR_SHAPE));
+    }
+  for (int d : {8, 16, 512, 1024, 100}) CHECK(kvq_qjl_supported(d, 64) == KVQ_ERR_SHAPE);
+  for (int m : {0, 16, 48, 288}) CHECK(kvq_qjl_supported(128, m) == KVQ_ERR_SHAPE);
+  uint16_t* sk = fake<uint16_t>(0x50000);
+  uint16_t* x = fake<uint16_t>(0x10000);
+  uint32_t* p = fake<uint32_t>(0x20000);
+  uint16_t* nr = fake<uint16_t>(0x40002);  // fp16 norms need 2-byte alignment only
+  kvq::g_stub = kvq::StubLog{};
+  CHECK(kvq_qjl_encode_pack(sk, 128, 96, x, 2, 4, 33, p, nr, 40, 7, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.qjl_calls == 1 && kvq::g_stub.m == 96 && kvq::g_stub.qjl.n_vec == 2 * 4 * 33);
+  CHECK(kvq::g_stub.qjl.map.contiguous == 0 && kvq::g_stub.qjl.map.S_cap == 40);
+  CHECK(kvq_qjl_encode_pack(sk, 128, 100, x, 2, 4, 33, p, nr, 40, 7, nullptr) == KVQ_ERR_SHAPE);
+  CHECK(kvq_qjl_encode_pack(sk, 128, 96, x, 2, 4, 33, p, nr, 40, 8, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_qjl_encode_pack(nullptr, 128, 96, x, 2, 4, 33, p, nr, 40, 7, nullptr) == KVQ_ERR_ARG);
+  CHECK(kvq_qjl_encode_pack(fake<uint16_t>(0x50008), 128, 96, x, 2, 4, 33, p, nr, 40, 7, nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq_qjl_encode_pack(sk, 128, 96, x, 2, 4, 33, p, fake<uint16_t>(0x40001), 40, 7, nullptr) == KVQ_ERR_ALIGN);
+}
+
+// ------------------------------------------------------------------------------ attention
+
+void test_attend() {
+  kvq_codebooks ck, cv, c3;
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &ck) == KVQ_OK);
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &cv) == KVQ_OK);
+  CHECK(kvq_build_codebooks(128, 3, nullptr, &c3) == KVQ_OK);
+  uint16_t* q = fake<uint16_t>(0x10000);
+  uint16_t* out = fake<uint16_t>(0x18000);
+  uint32_t* k1 = fake<uint32_t>(0x20000);
+  uint32_t* k2 = fake<uint32_t>(0x30000);
+  uint32_t* v1 = fake<uint32_t>(0x40000);
+  uint32_t* v2 = fake<uint32_t>(0x50000);
+  float* kn = fake<float>(0x60000);
+  float* vn = fake<float>(0x70000);
+  void* ws = fake<void>(0x100000);
+  struct Shape {
+    int64_t B, Hq, Sq, Hkv, S_cap, S_kv;
+  };
+  const Shape shapes[] = {{1, 32, 1, 8, 32768, 32768}, {2, 8, 3, 2, 1000, 999}, {1, 4, 1, 4, 5, 1},
+                          {3, 6, 2, 3, 70000, 65537}, {1, 1, 1, 1, 1 << 20, 1 << 20}};
+  for (int bits : {1, 2, 3, 4})
+    for (int d : {8, 64, 128, 1024})
+      for (const Shape& s : shapes) {
+        kvq_codebooks a, b;
+        CHECK(kvq_build_codebooks(d, bits, nullptr, &a) == KVQ_OK);
+        CHECK(kvq_build_codebooks(d, bits, nullptr, &b) == KVQ_OK);
+        int64_t need = -1;
+        CHECK(kvq_rvq_attend_workspace_size(d, bits, s.B, s.Hq, s.Sq, s.Hkv, s.S_kv, &need) == KVQ_OK);
+        CHECK(need > 0);
+        kvq::g_stub = kvq::StubLog{};
+        CHECK(kvq_rvq_attend(&a, &b, q, s.B, s.Hq, s.Sq, s.Hkv, k1, k2, kn, v1, v2, vn, s.S_cap, s.S_kv, 0.1f, ws,
+                             need, out, nullptr) == KVQ_OK);
+        const kvq::AttendArgs& p = kvq::g_stub.att;
+        CHECK(kvq::g_stub.attend_calls == 1);
+        CHECK(p.n_q == s.B * s.Hq * s.Sq && p.group == s.Hq / s.Hkv && p.Hkv == s.Hkv && p.Sq == s.Sq);
+        // the chunks cover the cached positions, none of them empty, within the combine's limit
+        CHECK(p.n_splits >= 1 && p.n_splits <= 4096 && p.chunk >= 1);
+        CHECK(static_cast<int64_t>(p.chunk) * p.n_splits >= s.S_kv);
+        CHECK(static_cast<int64_t>(p.chunk) * (p.n_splits - 1) < s.S_kv);
+        // one record of d + 4 floats per (query vector, chunk) fits the workspace
+        CHECK(p.n_q * p.n_splits * (d + 4) * 4 <= need);
+        CHECK(kvq_rvq_attend(&a, &b, q, s.B, s.Hq, s.Sq, s.Hkv, k1, k2, kn, v1, v2, vn, s.S_cap, s.S_kv, 0.1f, ws,
+                             need - 1, out, nullptr) == KVQ_ERR_RANGE);
+      }
+  int64_t need = 0;
+  CHECK(kvq_rvq_attend_workspace_size(128, 2, 1, 32, 1, 8, 4096, &need) == KVQ_OK);
+  const auto call = [&](const kvq_codebooks* a, const kvq_codebooks* b, int64_t Hq, int64_t Hkv, int64_t S_cap,
+                        int64_t S_kv, float scale, void* w, int64_t wb, uint16_t* o) {
+    return kvq_rvq_attend(a, b, q, 1, Hq, 1, Hkv, k1, k2, kn, v1, v2, vn, S_cap, S_kv, scale, w, wb, o, nullptr);
+  };
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_OK);
+  CHECK(call(&ck, &c3, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_SHAPE);   // different bits
+  CHECK(call(&ck, &cv, 30, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_SHAPE);   // Hq % Hkv
+  CHECK(call(&ck, &cv, 32, 8, 4095, 4096, 0.1f, ws, need, out) == KVQ_ERR_RANGE);   // S_kv > S_cap
+  CHECK(call(&ck, &cv, 32, 8, 4096, 0, 0.1f, ws, need, out) == KVQ_ERR_RANGE);      // S_kv < 1
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, NAN, ws, need, out) == KVQ_ERR_ARG);
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, INFINITY, ws, need, out) == KVQ_ERR_ARG);
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, 0.1f, nullptr, need, out) == KVQ_ERR_ARG);
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, 0.1f, fake<void>(0x100004), need, out) == KVQ_ERR_ALIGN);
+  CHECK(call(&ck, &cv, 32, 8, 4096, 4096, 0.1f, ws, need, fake<uint16_t>(0x18002)) == KVQ_ERR_ALIGN);
+  CHECK(call(nullptr, &cv, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_ARG);
+  CHECK(kvq_rvq_attend_workspace_size(128, 2, 1, 32, 1, 8, 4096, nullptr) == KVQ_ERR_ARG);
+  CHECK(kvq_rvq_attend_workspace_size(96, 2, 1, 32, 1, 8, 4096, &need) == KVQ_ERR_SHAPE);
+  CHECK(kvq_rvq_attend_workspace_size(128, 5, 1, 32, 1, 8, 4096, &need) == KVQ_ERR_SHAPE);
+  CHECK(kvq_rvq_attend_workspace_size(128, 2, 1, 32, 1, 8, 0, &need) == KVQ_ERR_RANGE);
+  // no query vectors: nothing to do, no pointer is looked at
+  kvq::g_stub = kvq::StubLog{};
+  CHECK(kvq_rvq_attend(&ck, &cv, nullptr, 0, 32, 1, 8, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4096,
+                       4096, 0.1f, nullptr, 0, nullptr, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.attend_calls == 0);
+}
+
+void test_status_text() {
+  for (int s = -7; s <= 2; ++s) CHECK(kvq_status_str(static_cast<kvq_status>(s)) != nullptr);
+}
+
+}  // namespace
+
+int main() {
+  test_codebooks();
+  test_encode_decode();
+  test_qjl();
+  test_attend();
+  test_status_text();
+  if (g_fail) {
+    std::fprintf(stderr, "%d checks failed\n", g_fail);
+    return 1;
+  }
+  std::printf("ok\n");
+  return 0;
+}
