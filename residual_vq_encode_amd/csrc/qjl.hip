@@ -126,7 +126,7 @@ __global__ __launch_bounds__(qjl_waves<D>() * 64) void qjl_encode_kernel(const Q
       for (int i = 0; i < 4; ++i) ss = dot2_f16<0>(w[i], w[i], ss);
     }
     ss += __shfl_xor(ss, 32);
-    const float nrm = __builtin_sqrtf(ss);
+    const float nrm = __builtin_amdgcn_sqrtf(ss);  // v_sqrt_f32, within 1 ulp (the fp16 result is held to 1e-6)
 
     // S x on the matrix cores, MBC M-blocks at a time (independent accumulators, k-steps
     // outermost), then their signs: register j of M-block mb is sketch dimension
