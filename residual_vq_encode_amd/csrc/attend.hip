@@ -196,18 +196,12 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
     for (int c = 0; c < CH; ++c) {
       const uint4 v = qp[c];
       const uint32_t xh[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {kPP ^ kx[q * (C / 2) + 4 * c], kPP ^ kx[q * (C / 2) + 4 * c + 1],
+                             kPP ^ kx[q * (C / 2) + 4 * c + 2], kPP ^ kx[q * (C / 2) + 4 * c + 3]};
+      float o[8];
+      dot2_stages8(xh, w, o);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint32_t w0 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * g];
-        const uint32_t w1 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * g + 1];
-        const float s0 = dot2_f16<0>(xh[2 * g], w0);
-        const float d0 = dot2_f16<1>(xh[2 * g], w0);
-        float* o = qs[k] + 8 * c + 4 * g;
-        o[0] = dot2_f16<0>(xh[2 * g + 1], w1, s0);
-        o[1] = dot2_f16<1>(xh[2 * g + 1], w1, d0);
-        o[2] = dot2_f16<2>(xh[2 * g + 1], w1, s0);
-        o[3] = dot2_f16<3>(xh[2 * g + 1], w1, d0);
-      }
+      for (int j = 0; j < 8; ++j) qs[k][8 * c + j] = o[j];
     }
     lane_stages<C, 4>(qs[k]);
     cross_stages<C, LOG_L>(qs[k], q);
@@ -441,8 +435,12 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
   constexpr int KS = D / 32;          // k-steps of the score product
   constexpr int CB = D / 16;          // 16-coordinate blocks of the value product
   static_assert(NWG >= 1 && D >= 64 && D <= 128, "matrix path: d = 64 or 128, d b >= 128");
-  using G = Layout<D>;                // prologue and epilogue: the codec's lane layout
-  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
+  // Prologue and epilogue: the codec's lane layout with 8 coordinates per lane, so a wave
+  // rotates VW = 512 / D query rows per pass and passes stop at the group's real rows (a GQA
+  // group of 4 takes one pass at d = 128 instead of rotating all 16 MFMA rows).
+  using G = Layout<D, 8>;
+  constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW;
+  constexpr int NPASS = kMfmaQ / VW;  // passes over the 16 rows
   constexpr int VT = kMfmaKeys * D;   // halfs per plane of the value tile
 
   // The block's LDS in one struct, small tables first: every table address is then a lane
@@ -488,9 +486,8 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
     const int64_t qi = qg * kMfmaQ + i;
     return (bb * Hq + hkv * a.group + qi / a.Sq) * a.Sq + qi % a.Sq;
   };
-  // the codec's lane layout for the queries (one pass: VW >= 16 at d <= 128)
-  static_assert(VW >= kMfmaQ, "one pass over the wave's queries");
-  const int q = lane & (L - 1), vl = lane >> LOG_L;
+  static_assert(C == 8 && NPASS * VW == kMfmaQ, "one 16-byte chunk of each query row per lane");
+  const int q = lane & (L - 1), vl = lane >> LOG_L;  // row p VW + vl of pass p, coordinates [8 q, 8 q + 8)
 
   // Positions, 32 per iteration: block k of 16 keys, lane (n, g) loads key 16 k + n's words of
   // its coordinate slice, and lane l the norms of key l % 32 (shared through LDS); the next
@@ -515,16 +512,15 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
     nvn = a.vn[rowbase + tn];
   };
 
-  // Before the block's tables are built, start the loads: this lane's part of query vl and
-  // the first positions.
-  uint4 qraw[CH];
+  // Before the block's tables are built, start the loads: this lane's part of query rows
+  // p VW + vl (zero past the group's nq rows) and the first positions.
+  uint4 qraw[NPASS];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) qraw[c] = make_uint4(0u, 0u, 0u, 0u);
+  for (int p = 0; p < NPASS; ++p) qraw[p] = make_uint4(0u, 0u, 0u, 0u);
   if (active) {
-    if (vl < nq) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) qraw[c] = reinterpret_cast<const uint4*>(a.q + qvec(vl) * D + q * C)[c];
-    }
+    for (int p = 0; p < NPASS; ++p)
+      if (p * VW + vl < nq) qraw[p] = reinterpret_cast<const uint4*>(a.q + qvec(p * VW + vl) * D + q * C)[0];
     fetch(t0);
   }
 
@@ -539,33 +535,23 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
   __syncthreads();
   if (!active) return;  // no barrier follows
 
-  // 1. Rotated queries y = H diag(s_k) q (scaled by qscale) into stage[16][D].
+  // 1. Rotated queries y = H diag(s_k) q (scaled by qscale) into stage[16][D]: rows below nq
+  //    rotated (their lanes past nq hold zeros), whole passes past nq written as zeros.
   {
     const float qk = (__builtin_popcount(q) & 1) ? -a.qscale : a.qscale;
-    float y[C];
+    const uint32_t w[4] = {kPP ^ kx[q * 4], kPP ^ kx[q * 4 + 1], kPP ^ kx[q * 4 + 2], kPP ^ kx[q * 4 + 3]};
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint32_t xh[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t w0 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * h];
-        const uint32_t w1 = kPP ^ kx[q * (C / 2) + 4 * c + 2 * h + 1];
-        const float s0 = dot2_f16<0>(xh[2 * h], w0);
-        const float d0 = dot2_f16<1>(xh[2 * h], w0);
-        float* o = y + 8 * c + 4 * h;
-        o[0] = dot2_f16<0>(xh[2 * h + 1], w1, s0);
-        o[1] = dot2_f16<1>(xh[2 * h + 1], w1, d0);
-        o[2] = dot2_f16<2>(xh[2 * h + 1], w1, s0);
-        o[3] = dot2_f16<3>(xh[2 * h + 1], w1, d0);
+    for (int p = 0; p < NPASS; ++p) {
+      float y[C] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (p * VW < nq) {  // wave-uniform
+        const uint32_t xh[4] = {qraw[p].x, qraw[p].y, qraw[p].z, qraw[p].w};
+        dot2_stages8(xh, w, y);
+        lane_stages<C, 4>(y);
+        cross_stages<C, LOG_L>(y, q);
       }
-    }
-    lane_stages<C, 4>(y);
-    cross_stages<C, LOG_L>(y, q);
-    if (vl < kMfmaQ) {
-      float4* dst = reinterpret_cast<float4*>(stage + vl * D + q * C);
-#pragma unroll
-      for (int c = 0; c < C / 4; ++c)
-        dst[c] = make_float4(y[4 * c] * qk, y[4 * c + 1] * qk, y[4 * c + 2] * qk, y[4 * c + 3] * qk);
+      float4* dst = reinterpret_cast<float4*>(stage + (p * VW + vl) * D + q * C);
+      dst[0] = make_float4(y[0] * qk, y[1] * qk, y[2] * qk, y[3] * qk);
+      dst[1] = make_float4(y[4] * qk, y[5] * qk, y[6] * qk, y[7] * qk);
     }
   }
   wave_lds_fence();
@@ -749,24 +735,18 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
     ws[0] = m;
     ws[1] = l;
   }
-  {
-    const int q = lane & (L - 1), vl = lane >> LOG_L;
 #pragma unroll
-    for (int p0 = 0; p0 < kMfmaQ; p0 += VW) {
-      const int i = p0 + vl;
-      float z[C];
-#pragma unroll
-      for (int c = 0; c < C / 4; ++c) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < kMfmaQ) v = reinterpret_cast<const float4*>(stage + i * D + q * C)[c];
-        z[4 * c] = v.x; z[4 * c + 1] = v.y; z[4 * c + 2] = v.z; z[4 * c + 3] = v.w;
-      }
-      unrotate_f32<D, 32>(z, q, a.inv_sqrt_d, vsg);
-      if (i < nq) {
-        float4* wa = reinterpret_cast<float4*>(a.ws + (qvec(i) * a.n_splits + sp) * (D + 4) + 4 + q * C);
-#pragma unroll
-        for (int c = 0; c < C / 4; ++c) wa[c] = make_float4(z[4 * c], z[4 * c + 1], z[4 * c + 2], z[4 * c + 3]);
-      }
+  for (int p = 0; p < NPASS; ++p) {
+    if (p * VW >= nq) break;  // wave-uniform: the group's rows are done
+    const int i = p * VW + vl;
+    const float4 v0 = reinterpret_cast<const float4*>(stage + i * D + q * C)[0];
+    const float4 v1 = reinterpret_cast<const float4*>(stage + i * D + q * C)[1];
+    float z[C] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    unrotate_f32<D, 8>(z, q, a.inv_sqrt_d, vsg);
+    if (i < nq) {
+      float4* wa = reinterpret_cast<float4*>(a.ws + (qvec(i) * a.n_splits + sp) * (D + 4) + 4 + q * C);
+      wa[0] = make_float4(z[0], z[1], z[2], z[3]);
+      wa[1] = make_float4(z[4], z[5], z[6], z[7]);
     }
   }
 }

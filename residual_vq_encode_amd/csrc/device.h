@@ -78,35 +78,37 @@ constexpr int kNonTemporal = 2;
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// fp16x2 dot products with a float32 addend, the non-accumulating (VOP3P) form: the
-// compiler otherwise picks the accumulating v_dot2c and spends a move zeroing each
-// destination. `w` holds two fp16 weights (low half weighs the pair's first element);
-// NEG selects the VOP3P source modifiers applied to it: 0 = (w0, w1), 1 = (w0, -w1),
-// 2 = (-w0, -w1), 3 = (-w0, w1). With w = (s_a, s_b), the rotation's signs for the pair,
-// this multiplies the pair by (+-s_a, +-s_b) exactly: the sign flip costs nothing.
+// Butterfly stages 1 and 2 of 8 coordinates straight from their fp16 pairs: xh[k] holds
+// coordinates (2k, 2k + 1) and w[k] the fp16 weights (s_2k, s_2k+1), the rotation's signs for
+// that pair. v_dot2_f32_f16 multiplies a pair by the weights exactly and adds a float32
+// addend; its VOP3P neg_lo / neg_hi modifiers flip the weights' signs for free, so each
+// 4-coordinate group takes 6 instructions: s = P0.(w0, w1), d = P0.(w0, -w1), then
+// P1.(w2, w3) + s, P1.(w2, -w3) + d, P1.(-w2, -w3) + s, P1.(-w2, w3) + d.
+// The twelve instructions are one asm block ending in s_nop 2: on gfx950 a VALU instruction
+// reading a DOT result needs 3 wait states, which the compiler inserts for its own dot
+// instructions but cannot know about for inline asm. (Inside the block the partial sums are
+// read only as the addend of the same opcode, which needs none.) Written as asm because the
+// compiler otherwise picks the accumulating v_dot2c and spends a move per product.
 constexpr uint32_t kPP = 0x3C003C00u;  // fp16 (+1, +1)
 
-template <int NEG>
-__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w) {
-  float r;
-  if constexpr (NEG == 0) asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(pair), "v"(w));
-  if constexpr (NEG == 1) asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
-  if constexpr (NEG == 2)
-    asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_lo:[0,1,0] neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
-  if constexpr (NEG == 3) asm("v_dot2_f32_f16 %0, %1, %2, 0 neg_lo:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w));
-  return r;
-}
-template <int NEG>
-__device__ __forceinline__ float dot2_f16(uint32_t pair, uint32_t w, float addend) {
-  float r;
-  if constexpr (NEG == 0) asm("v_dot2_f32_f16 %0, %1, %2, %3" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
-  if constexpr (NEG == 1)
-    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
-  if constexpr (NEG == 2)
-    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_lo:[0,1,0] neg_hi:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
-  if constexpr (NEG == 3)
-    asm("v_dot2_f32_f16 %0, %1, %2, %3 neg_lo:[0,1,0]" : "=v"(r) : "v"(pair), "v"(w), "v"(addend));
-  return r;
+__device__ __forceinline__ void dot2_stages8(const uint32_t (&xh)[4], const uint32_t (&w)[4], float (&o)[8]) {
+  float s0, d0, s1, d1;
+  asm("v_dot2_f32_f16 %8, %12, %16, 0\n"
+      "v_dot2_f32_f16 %9, %12, %16, 0 neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %10, %14, %18, 0\n"
+      "v_dot2_f32_f16 %11, %14, %18, 0 neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %0, %13, %17, %8\n"
+      "v_dot2_f32_f16 %1, %13, %17, %9 neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %2, %13, %17, %8 neg_lo:[0,1,0] neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %3, %13, %17, %9 neg_lo:[0,1,0]\n"
+      "v_dot2_f32_f16 %4, %15, %19, %10\n"
+      "v_dot2_f32_f16 %5, %15, %19, %11 neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %6, %15, %19, %10 neg_lo:[0,1,0] neg_hi:[0,1,0]\n"
+      "v_dot2_f32_f16 %7, %15, %19, %11 neg_lo:[0,1,0]\n"
+      "s_nop 2"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(s0), "=&v"(d0), "=&v"(s1), "=&v"(d1)
+      : "v"(xh[0]), "v"(xh[1]), "v"(xh[2]), "v"(xh[3]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
 }
 
 // The value held by lane (lane ^ M). M = 1, 2: DPP quad permutes; M = 8: DPP row rotate

@@ -149,17 +149,11 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
         const half2_t h = __builtin_bit_cast(half2_t, xh[i]);
         acc[i] = __builtin_amdgcn_fdot2(h, h, acc[i], false);
       }
+      const uint32_t w[4] = {wt[4 * c], wt[4 * c + 1], wt[4 * c + 2], wt[4 * c + 3]};
+      float o[8];
+      dot2_stages8(xh, w, o);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const uint32_t w0 = wt[4 * c + 2 * g], w1 = wt[4 * c + 2 * g + 1];
-        const float s0 = dot2_f16<0>(xh[2 * g], w0);
-        const float d0 = dot2_f16<1>(xh[2 * g], w0);
-        float* o = y + 8 * c + 4 * g;
-        o[0] = dot2_f16<0>(xh[2 * g + 1], w1, s0);
-        o[1] = dot2_f16<1>(xh[2 * g + 1], w1, d0);
-        o[2] = dot2_f16<2>(xh[2 * g + 1], w1, s0);
-        o[3] = dot2_f16<3>(xh[2 * g + 1], w1, d0);
-      }
+      for (int j = 0; j < 8; ++j) y[8 * c + j] = o[j];
     }
     wait_lds();
 

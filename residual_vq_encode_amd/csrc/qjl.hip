@@ -123,7 +123,13 @@ __global__ __launch_bounds__(qjl_waves<D>() * 64) void qjl_encode_kernel(const Q
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t w = __builtin_bit_cast(u32x4_t, b[ks]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ss = dot2_f16<0>(w[i], w[i], ss);
+      for (int i = 0; i < 4; ++i) {
+        // through a scalar: bit-casting the vector element w[i] directly compiled to w[0]
+        // for every i
+        const uint32_t e = w[i];
+        const half2_t p = __builtin_bit_cast(half2_t, e);
+        ss = __builtin_amdgcn_fdot2(p, p, ss, false);
+      }
     }
     ss += __shfl_xor(ss, 32);
     const float nrm = __builtin_amdgcn_sqrtf(ss);  // v_sqrt_f32, within 1 ulp (the fp16 result is held to 1e-6)
