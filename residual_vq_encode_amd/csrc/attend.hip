@@ -514,14 +514,27 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
 
   // Before the block's tables are built, start the loads: this lane's part of query rows
   // p VW + vl (zero past the group's nq rows) and the first positions.
+  // The chunk records this lane writes at the end (row p VW + vl of each pass, and the header
+  // of query n for lanes g = 0) are located here, where the index arithmetic hides behind
+  // the loads, rather than on the epilogue's critical path.
   uint4 qraw[NPASS];
+  int64_t rec[NPASS];
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p) qraw[p] = make_uint4(0u, 0u, 0u, 0u);
+  for (int p = 0; p < NPASS; ++p) {
+    qraw[p] = make_uint4(0u, 0u, 0u, 0u);
+    rec[p] = 0;
+  }
+  int64_t hdr = 0;
   if (active) {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-      if (p * VW + vl < nq) qraw[p] = reinterpret_cast<const uint4*>(a.q + qvec(p * VW + vl) * D + q * C)[0];
+      if (p * VW < nq && p * VW + vl < nq) {
+        const int64_t qv = qvec(p * VW + vl);
+        qraw[p] = reinterpret_cast<const uint4*>(a.q + qv * D + q * C)[0];
+        rec[p] = (qv * a.n_splits + sp) * (D + 4) + 4 + q * C;
+      }
     fetch(t0);
+    if (n < nq) hdr = (qvec(n) * a.n_splits + sp) * (D + 4);
   }
 
   fill_mfma_table<BITS>(a.ztab_k, tabk);
@@ -731,7 +744,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
         make_float4(acc[cb][0] * back, acc[cb][1] * back, acc[cb][2] * back, acc[cb][3] * back);
   wave_lds_fence();
   if (g == 0 && n < nq) {
-    float* ws = a.ws + (qvec(n) * a.n_splits + sp) * (D + 4);
+    float* ws = a.ws + hdr;
     ws[0] = m;
     ws[1] = l;
   }
@@ -744,7 +757,7 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
     float z[C] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     unrotate_f32<D, 8>(z, q, a.inv_sqrt_d, vsg);
     if (i < nq) {
-      float4* wa = reinterpret_cast<float4*>(a.ws + (qvec(i) * a.n_splits + sp) * (D + 4) + 4 + q * C);
+      float4* wa = reinterpret_cast<float4*>(a.ws + rec[p]);
       wa[0] = make_float4(z[0], z[1], z[2], z[3]);
       wa[1] = make_float4(z[4], z[5], z[6], z[7]);
     }
