@@ -417,6 +417,50 @@ __device__ __forceinline__ void table_operand(const uint32_t (&lo)[NWG], const u
   }
 }
 
+// The key operand of one score MFMA: the lane's coordinates 4 J .. 4 J + 3 (of its slice) as
+// 8 fp16 k-slots holding each coordinate's hi and lo parts, taken from the table entries
+// as they are: (hi 01, lo 01, hi 23, lo 23) at b = 2, (hi 01, hi 23, lo 01, lo 23) at b = 1,
+// (hi 0, lo 0, hi 1, lo 1, ...) at b = 4. The query operands repeat each coordinate's hi
+// (and, in the second product, lo) part in the matching slots, so two MFMAs give the exact
+// product of the split key and query values with no operand shuffling.
+template <int BITS, int NWG, int J>
+__device__ __forceinline__ u32x4_t key_operand(const uint32_t (&lo)[NWG], const uint32_t (&hi)[NWG],
+                                               const uint32_t* tab) {
+  constexpr int P = 4 / BITS;
+  auto idx = [&](int t) -> uint32_t { return (((t & 1) ? hi[t >> 3] : lo[t >> 3]) >> (8 * ((t & 7) >> 1))) & 0xFFu; };
+  if constexpr (P == 2) {
+    const uint2 e0 = reinterpret_cast<const uint2*>(tab)[idx(2 * J)];
+    const uint2 e1 = reinterpret_cast<const uint2*>(tab)[idx(2 * J + 1)];
+    return u32x4_t{e0.x, e0.y, e1.x, e1.y};
+  } else if constexpr (P == 4) {
+    const uint4 e = reinterpret_cast<const uint4*>(tab)[idx(J)];
+    return u32x4_t{e.x, e.y, e.z, e.w};
+  } else {
+    return u32x4_t{tab[idx(4 * J)], tab[idx(4 * J + 1)], tab[idx(4 * J + 2)], tab[idx(4 * J + 3)]};
+  }
+}
+
+// The query operands for key_operand's slots: p0, p1 are the (hi, lo) fp16 pairs of the
+// coordinates (4 J, 4 J + 1) and (4 J + 2, 4 J + 3); h selects the hi (0) or lo (1) parts.
+template <int BITS>
+__device__ __forceinline__ u32x4_t query_operand(uint2 p0, uint2 p1, int h) {
+  constexpr int P = 4 / BITS;
+  const uint32_t a = h ? p0.y : p0.x, b = h ? p1.y : p1.x;
+  if constexpr (P == 2) {
+    return u32x4_t{a, a, b, b};
+  } else if constexpr (P == 4) {
+    return u32x4_t{a, b, a, b};
+  } else {  // each slot pair holds one coordinate's (hi, lo): repeat that coordinate's part
+    return u32x4_t{(a & 0xFFFFu) * 0x10001u, (a >> 16) * 0x10001u, (b & 0xFFFFu) * 0x10001u, (b >> 16) * 0x10001u};
+  }
+}
+
+__device__ __forceinline__ f32x4_t mfma2(const u32x4_t& a, const u32x4_t& b1, const u32x4_t& b2, f32x4_t c) {
+  const f16x8_t A = __builtin_bit_cast(f16x8_t, a);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8_t, b1), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(f16x8_t, b2), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma3(const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh, const u32x4_t& bl,
                                          f32x4_t c) {
   const f16x8_t Ah = __builtin_bit_cast(f16x8_t, ah), Al = __builtin_bit_cast(f16x8_t, al);
@@ -571,7 +615,8 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
 
   // 2. Query operands: lane (n, g) takes query n's coordinates [CPL g, CPL g + CPL), divided by
   //    the query's largest magnitude qn (0 for padding queries).
-  u32x4_t qh[KS], ql[KS];
+  constexpr int HS = CPL / 4;  // score MFMA pairs per key block: 4 coordinates of the lane each
+  u32x4_t qb1[HS], qb2[HS];
   float qn;
   {
     float qv[CPL];
@@ -588,13 +633,12 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
     qn = mx;
     const float inv = mx > 0.f ? 1.0f / mx : 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint2 hl = split_pair(qv[8 * s + 2 * k] * inv, qv[8 * s + 2 * k + 1] * inv);
-        qh[s][k] = hl.x;
-        ql[s][k] = hl.y;
-      }
+    for (int j = 0; j < HS; ++j) {
+      const uint2 p0 = split_pair(qv[4 * j] * inv, qv[4 * j + 1] * inv);
+      const uint2 p1 = split_pair(qv[4 * j + 2] * inv, qv[4 * j + 3] * inv);
+      qb1[j] = query_operand<BITS>(p0, p1, 0);
+      qb2[j] = query_operand<BITS>(p0, p1, 1);
+    }
   }
   wave_lds_fence();
 
@@ -639,10 +683,9 @@ __global__ __launch_bounds__(kBlockThreads, 2) void attend_mfma(const AttendArgs
       uint32_t lo[NWG], hi[NWG];
       nibble_bytes<NWG>(k1[k], k2[k], lo, hi);
       sc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      static_for<0, KS>([&](auto si) {
-        u32x4_t ah, al;
-        table_operand<BITS, NWG, decltype(si)::value>(lo, hi, tabk, ah, al);
-        sc[k] = mfma3(ah, al, qh[decltype(si)::value], ql[decltype(si)::value], sc[k]);
+      static_for<0, HS>([&](auto ji) {
+        constexpr int J = decltype(ji)::value;
+        sc[k] = mfma2(key_operand<BITS, NWG, J>(lo, hi, tabk), qb1[J], qb2[J], sc[k]);
       });
     }
 
