@@ -289,9 +289,12 @@ def main() -> int:
     from oracle import codebooks as ocb
     from oracle import flips, rvq
     j = (args.warmup + K - 1) % P
-    # a strided sample of 65536 vectors (the whole tensor when smaller): the flip cap is a
-    # rate, and a sample of ~10^7 codes estimates it without small-sample noise
-    idx = torch.arange(0, n_vec, max(1, n_vec // 65536))
+    # a strided sample (the whole tensor when smaller): the flip cap is a rate. At b <= 2
+    # flips are rare and 65536 vectors suffice; at b >= 3 the float32 transform leaves about
+    # 5e-7 of the codes flipped next to a boundary, so the sample takes 2^18 vectors (67M
+    # codes, a count of ~35 against a cap of 67) for its count to resolve the rate
+    n_check = 65536 if bits <= 2 else 262144
+    idx = torch.arange(0, n_vec, max(1, n_vec // n_check))[:n_check]
     rows = xs[j].reshape(-1, D)[idx.to(dev)].cpu().numpy()
     t = ocb.build_tables(D, bits)
     dev_p1 = p1s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)

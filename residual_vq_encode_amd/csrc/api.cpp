@@ -70,38 +70,52 @@ RowMap row_map(int64_t S, int64_t S_cap, int64_t s_offset) {
   return m;
 }
 
-// Bucket table for the positive thresholds of one stage (bits >= 3). The bucket width is
-// 0.9 of the smallest gap between consecutive thresholds (0 included), so every bucket
-// [j, j+1) in table units holds at most one threshold; thresholds are the float32 values
-// RN32(t_k * unit) and m_base(j) counts those below j, so m = m_base + [u > thr] counts
-// every threshold below u exactly.
+// Bucket table of one stage (bits >= 3). The kernel scales a value t (true units) to the
+// float32 w = t / (2R), compares it in that form, and reads entry
+// j = RNE(v * sub * kTabBuckets) / sub of v = clamp(RN32(w + 1/2), 0, 1) (see kTabBuckets).
+// Every v that reaches entry j lies in [(sub j - 1/2), (sub j + sub - 1/2)] / (sub * kTabBuckets)
+// (ties either way), so every w that does lies in that interval shifted by -1/2 and widened
+// by the rounding of w + 1/2 (at most 2^-24; 2^-23 is allowed), or beyond the end of [-1/2,
+// 1/2] for the two end entries. With the thresholds as float32 values tw_k = RN32(b_k / (2R)),
+// base_j counts those below the widened interval and thr_j is the one inside it (+inf if
+// none), so that
+// base_j + [w > thr_j] = #{k : w > tw_k}, the count of boundaries the value exceeds taken in
+// float32 on w. Fails if a bucket would hold two thresholds or they are not increasing.
 struct Buckets {
-  double unit;               // table units per true unit
-  int jmax;                  // last bucket; its entry has every threshold below it
-  float thr[48];
-  int32_t mbase[48];
+  double two_r;  // 2R: true units per unit of w
+  float thr[kvq::kTabEntries];
+  int32_t base[kvq::kTabEntries];
 };
 
-bool make_buckets(const float* bnd, int bits, Buckets* bk, int max_entries) {
-  const int half = 1 << (bits - 1);
-  const int nt = half - 1;                 // positive thresholds b[half .. 2*half - 2]
-  const float* t = bnd + half;
-  double gap = t[0];
-  for (int k = 1; k < nt; ++k) gap = std::fmin(gap, static_cast<double>(t[k]) - t[k - 1]);
-  bk->unit = 1.0 / (0.9 * gap);
-  float tf[8];
-  for (int k = 0; k < nt; ++k) tf[k] = static_cast<float>(static_cast<double>(t[k]) * bk->unit);
-  bk->jmax = static_cast<int>(std::floor(tf[nt - 1])) + 1;
-  if (bk->jmax + 1 > max_entries) return false;
-  for (int j = 0; j <= bk->jmax; ++j) {
-    int below = 0;
-    float inside = std::numeric_limits<float>::max();
+bool make_buckets(const float* bnd, int bits, int sub, double inv_sqrt_d, Buckets* bk) {
+  const int nt = (1 << bits) - 1;
+  double tmax = 0.0;
+  for (int k = 0; k < nt; ++k) {
+    if (!std::isfinite(bnd[k]) || (k > 0 && !(bnd[k] > bnd[k - 1]))) return false;
+    tmax = std::fmax(tmax, std::fabs(static_cast<double>(bnd[k])));
+  }
+  if (!(tmax > 0.0)) return false;
+  // thresholds land in about [-0.45, 0.45]; 2R is adjusted so that the kernel's scale
+  // 1 / (sqrt(d) 2R) is a float32 value exactly (one rounding less in every decision)
+  bk->two_r = inv_sqrt_d / static_cast<double>(static_cast<float>(inv_sqrt_d / (2.25 * tmax)));
+  float tw[15];
+  for (int k = 0; k < nt; ++k) tw[k] = static_cast<float>(static_cast<double>(bnd[k]) / bk->two_r);
+  const double step = 1.0 / (static_cast<double>(sub) * kvq::kTabBuckets), slack = std::ldexp(1.0, -23);
+  for (int j = 0; j < kvq::kTabEntries; ++j) {
+    const double lo = (sub * j - 0.5) * step - 0.5 - slack, hi = (sub * j + sub - 0.5) * step - 0.5 + slack;
+    int below = 0, inside = 0;
+    float thr = std::numeric_limits<float>::infinity();
     for (int k = 0; k < nt; ++k) {
-      if (tf[k] < static_cast<float>(j)) ++below;
-      else if (tf[k] < static_cast<float>(j + 1)) inside = tf[k];
+      if (static_cast<double>(tw[k]) < lo) {
+        ++below;
+      } else if (static_cast<double>(tw[k]) <= hi) {
+        ++inside;
+        thr = tw[k];
+      }
     }
-    bk->thr[j] = inside;
-    bk->mbase[j] = below;
+    if (inside > 1) return false;
+    bk->thr[j] = thr;
+    bk->base[j] = below;
   }
   return true;
 }
@@ -113,12 +127,12 @@ float as_float(int32_t v) {
 }
 
 kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
-  const int d = cb->d, bits = cb->bits, k = 1 << bits, half = k / 2;
+  const int d = cb->d, bits = cb->bits;
   const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
   std::memset(a->xmask, 0, sizeof(a->xmask));
   std::memset(a->tab1, 0, sizeof(a->tab1));
   std::memset(a->tab2, 0, sizeof(a->tab2));
-  a->j1max = a->j2max = 0;
+  a->k2_scale = 0.f;
   a->cm2[0] = a->cm2[1] = 0.f;
   if (bits == 1) {
     a->k_scale = static_cast<float>(inv_sqrt_d);  // NX = -y_true
@@ -131,23 +145,22 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
     a->cm2[0] = static_cast<float>((static_cast<double>(cb->c1[3]) - cb->c1[2]) / T2);  // h in units 2/T2
   } else {
     Buckets b1, b2;
-    if (!make_buckets(cb->b1, bits, &b1, kvq::kTab1Max) || !make_buckets(cb->b2, bits, &b2, kvq::kTab2Max))
+    if (!make_buckets(cb->b1, bits, 16, inv_sqrt_d, &b1) || !make_buckets(cb->b2, bits, 8, inv_sqrt_d, &b2))
       return KVQ_ERR_ARG;
-    a->k_scale = static_cast<float>(b1.unit * inv_sqrt_d);
-    a->r12 = static_cast<float>(b2.unit / b1.unit);
-    a->j1max = b1.jmax;
-    a->j2max = b2.jmax;
-    for (int j = 0; j <= b1.jmax; ++j) {
-      const int m = b1.mbase[j];
-      const bool has = b1.thr[j] != std::numeric_limits<float>::max();
+    a->k_scale = static_cast<float>(inv_sqrt_d / b1.two_r);
+    a->k2_scale = static_cast<float>(inv_sqrt_d / b2.two_r);
+    a->r12 = 0.f;
+    // stage 2 compares w2 = y_true / (2 R2) + (-c1[m] / (2 R2)) for stage-1 code m
+    auto offset2 = [&](int m) { return static_cast<float>(-static_cast<double>(cb->c1[m]) / b2.two_r); };
+    for (int j = 0; j < kvq::kTabEntries; ++j) {
+      const int m = b1.base[j];
+      const bool has = b1.thr[j] != std::numeric_limits<float>::infinity();
       a->tab1[j][0] = b1.thr[j];
       a->tab1[j][1] = as_float(m);
-      a->tab1[j][2] = static_cast<float>(cb->c1[half + m] * b2.unit);
-      a->tab1[j][3] = static_cast<float>(cb->c1[half + (has ? m + 1 : m)] * b2.unit);
-    }
-    for (int j = 0; j <= b2.jmax; ++j) {
+      a->tab1[j][2] = offset2(m);
+      a->tab1[j][3] = offset2(has ? m + 1 : m);
       a->tab2[j][0] = b2.thr[j];
-      a->tab2[j][1] = as_float(b2.mbase[j]);
+      a->tab2[j][1] = as_float(b2.base[j]);
     }
   }
   for (int m = 0; m < d / 2; ++m)

@@ -69,18 +69,23 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
   constexpr bool STAGED = BITS == 3 && L > 1;        // 10-code words straddle lanes
   // words stored per lane: STAGED lanes store the (3 or 4) words that start in their slice
   constexpr int NWL = STAGED ? 4 : (L == 1 ? NW : C / EPW);
-  constexpr int HALFM1 = (1 << (BITS - 1)) - 1;
   constexpr bool TWO = STAGES == 2;                  // stage 2 computed and stored
   static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
   static_assert(!STAGED || C == 32, "a 3-bit lane slice is 96 bits");
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
-  __shared__ float4 t1s[BITS >= 3 ? kTab1Max : 1];
-  __shared__ float2 t2s[BITS >= 3 ? kTab2Max : 1];
+  // bucket tables (BITS >= 3): 128 slots, every offset the 7-bit masks can form; the slots
+  // past the last entry are never reached by a v in [0, 1] and hold "no threshold"
+  constexpr int TSLOTS = BITS >= 3 ? 128 : 1;
+  __shared__ float4 t1s[TSLOTS];
+  __shared__ float2 t2s[TSLOTS];
   if constexpr (BITS >= 3) {
-    for (int i = threadIdx.x; i < kTab1Max; i += kBlockThreads)
-      t1s[i] = make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3]);
-    for (int i = threadIdx.x; i < kTab2Max; i += kBlockThreads) t2s[i] = make_float2(a.tab2[i][0], a.tab2[i][1]);
+    for (int i = threadIdx.x; i < TSLOTS; i += kBlockThreads) {
+      const bool in = i < kTabEntries;
+      t1s[i] = in ? make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3])
+                  : make_float4(__builtin_inff(), 0.f, 0.f, 0.f);
+      t2s[i] = in ? make_float2(a.tab2[i][0], a.tab2[i][1]) : make_float2(__builtin_inff(), 0.f);
+    }
   }
   __syncthreads();
 
@@ -193,7 +198,8 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     // per tile for denormal scaling and the last-bit fix-up. The sum of squares of fp16 values
     // is 0 or a normal float32, and the stored norm is held to 1e-6 relative, so neither is
     // needed.
-    const float n = __builtin_amdgcn_sqrtf(lane_sum<LOG_L>((acc[0] + acc[1]) + (acc[2] + acc[3])));
+    const float ss = lane_sum<LOG_L>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    const float n = __builtin_amdgcn_sqrtf(ss);
     __builtin_amdgcn_sched_barrier(0);
 
     // 4. Quantize both stages and pack. K maps the raw transform to the stage-1 unit with
@@ -202,7 +208,23 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     //    (the count semantics at the middle boundary 0). A zero vector gets K = 0, so
     //    y_true = 0. The stage-2 value X2 = (|y_true| - cm) * unit2 is formed from y'
     //    directly (K2 = |K| * r12), one rounding.
-    float K = (n > 0.f) ? a.k_scale * __builtin_amdgcn_rcpf(n) : 0.f;  // v_rcp_f32: 1 ulp
+    //    BITS >= 3 compare w1 = fma(y', K, +0) = y_true / (2 R1) and
+    //    w2 = fma(y', K2s, -c1[m] / (2 R2)) = (y_true - c1[m]) / (2 R2) (K2s carries the lane's
+    //    sign as K does) with thresholds in the same units: an exact zero gives w1 = +0, which
+    //    does not exceed the middle threshold 0.
+    //    BITS >= 3 take both scales as RN32(k / sqrt(ss)), through v_rsq_f64: the stage-2
+    //    decision on y_true - c1[m] carries |y_true| times the scale's relative error, which
+    //    the finer codes turn into flips at their boundaries; the float32 chain (square
+    //    root, reciprocal, product) would round three times.
+    float K, K2s = 0.f;
+    if constexpr (BITS >= 3) {
+      const double r = (ss > 0.f) ? __builtin_amdgcn_rsq(static_cast<double>(ss)) : 0.0;
+      K = static_cast<float>(static_cast<double>(a.k_scale) * r);
+      K2s = static_cast<float>(static_cast<double>(a.k2_scale) * r);
+      if (negated) K2s = -K2s;
+    } else {
+      K = (n > 0.f) ? a.k_scale * __builtin_amdgcn_rcpf(n) : 0.f;  // v_rcp_f32: 1 ulp
+    }
     const float K2 = K * a.r12;
     if (negated) K = -K;
     // Codes of this lane's coordinates [jlo, jhi) of both stages, LSB-first with code jlo in
@@ -232,19 +254,21 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
           const float w = __builtin_fmaf(__builtin_fabsf(u), a.r12, -a.cm2[0]);
           u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(w), 30);
         } else {
-          // bucket tables: m = number of positive thresholds below |y|, in table units
-          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
-          const int j1 = static_cast<int>(__builtin_fminf(ax, static_cast<float>(a.j1max)));
-          const float4 e = t1s[j1];
-          const bool gt = ax > e.x;
-          u1 = (u1 << (BITS - 1)) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
-          const float cm = gt ? e.w : e.z;
-          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -cm);
-          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
-          const float ax2 = __builtin_fabsf(x2);
-          const int j2 = static_cast<int>(__builtin_fminf(ax2, static_cast<float>(a.j2max)));
-          const float2 e2 = t2s[j2];
-          u2 = (u2 << (BITS - 1)) | (__float_as_uint(e2.y) + (ax2 > e2.x ? 1u : 0u));
+          // Bucket tables: the code is base + [w > thr] of the entry that the bucket of
+          // v = clamp(w + 1/2, 0, 1) selects (the clamp is the add's output modifier). The
+          // entry's byte offset is read from the bits of v + 2^13 (spacing 2^-10: sixteen
+          // times the bucket count) and of v2 + 2^14 (spacing 2^-9, eight-byte entries).
+          const float w1 = __builtin_fmaf(y[j], K, 0.0f);
+          const float v1 = __builtin_amdgcn_fmed3f(w1 + 0.5f, 0.0f, 1.0f);
+          const uint32_t o1 = __float_as_uint(v1 + 8192.0f) & 0x7F0u;
+          const float4 e = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(t1s) + o1);
+          const bool gt = w1 > e.x;
+          u1 = (u1 << BITS) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
+          const float w2 = __builtin_fmaf(y[j], K2s, gt ? e.w : e.z);
+          const float v2 = __builtin_amdgcn_fmed3f(w2 + 0.5f, 0.0f, 1.0f);
+          const uint32_t o2 = __float_as_uint(v2 + 16384.0f) & 0x3F8u;
+          const float2 e2 = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(t2s) + o2);
+          u2 = (u2 << BITS) | (__float_as_uint(e2.y) + (w2 > e2.x ? 1u : 0u));
         }
       }
       // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
@@ -253,22 +277,16 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
       // downward from the middle: its low bits are (2^(BITS-1) - 1) - m = m xor
       // (2^(BITS-1) - 1); at BITS = 2 that low bit is O xor P xor 1 from the [>= T] bit the
       // alignbit stored.
+      // (BITS >= 3 fields are the codes themselves.)
       const uint32_t ones = field_ones<BITS>(cnt);
-      const uint32_t hi = ones << (BITS - 1);
       if constexpr (BITS == 2) {
         // stage 2 holds (sign(W), [|W| >= 2]); its residual-magnitude sign is
         // Q = sign(U) xor sign(W) with sign(U) = not O, so P2 = P xor not O xor sign(W)
         u2 ^= ((u1 ^ (u1 >> 1) ^ ones) & ones) << 1;
         u1 ^= ~(u1 >> 1) & ones;
         u2 ^= ~(u2 >> 1) & ones;
-      } else {
-        u2 ^= u1 & hi;
-      }
-      if constexpr (BITS >= 3) {
-        const uint32_t n1 = ~(u1 >> (BITS - 1)) & ones;
-        const uint32_t n2 = ~(u2 >> (BITS - 1)) & ones;
-        u1 ^= n1 * static_cast<uint32_t>(HALFM1);
-        u2 ^= n2 * static_cast<uint32_t>(HALFM1);
+      } else if constexpr (BITS == 1) {
+        u2 ^= u1;
       }
       if constexpr (STAGES == 0) u1 = ~u1 & ones;
       w1o = u1;

@@ -13,8 +13,16 @@ namespace kvq {
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
-constexpr int kTab1Max = 24;  // stage-1 bucket table entries (bits >= 3)
-constexpr int kTab2Max = 40;  // stage-2 bucket table entries (bits >= 3)
+// Bucket tables of the 3- and 4-bit quantizers. A value t of either stage is scaled to
+// w = t / (2R) (R: a little more than the stage's largest threshold magnitude), compared
+// in that form, and located through v = clamp(w + 1/2, 0, 1): the entry is
+// RNE(v * kTabSub * kTabBuckets) / kTabSub, i.e. the kTabBuckets + 1 entries split [0, 1]
+// evenly. The integer is taken from the float32 bits of v + 2^e, whose spacing is
+// 1 / (kTabSub * kTabBuckets) in [2^e, 2^(e+1)): masked, they are the entry's byte offset.
+// Stage 1 entries are 16 bytes (kTabSub = 16, e = 13), stage 2 entries 8 bytes (kTabSub = 8,
+// e = 14).
+constexpr int kTabBuckets = 64;
+constexpr int kTabEntries = kTabBuckets + 1;
 
 // Where token s of (b, h) lands in a cache whose token axis has capacity S_cap:
 // row(v) = (v / S) * S_cap + s_offset + v % S for the flattened input index v.
@@ -32,17 +40,21 @@ struct EncodeArgs {
   int64_t n_vec;
   RowMap map;
   // Per-vector scale: the quantizer works on X = y_true * unit, and the kernel forms
-  // -X = fma(y', -k_scale / n, +0) from the raw transform y' = H diag(s) x.
+  // -X = fma(y', -k_scale / n, +0) from the raw transform y' = H diag(s) x (bits <= 2);
+  // bits >= 3: w1 = fma(y', k_scale / n, +0) = y_true / (2 R1) (R1 chosen so that
+  // k_scale = 1 / (sqrt(d) 2 R1) is exact).
   float k_scale;
-  float r12;          // stage-2 units per stage-1 unit
+  float r12;          // stage-2 units per stage-1 unit (bits <= 2)
+  float k2_scale;     // bits >= 3: w2 = fma(y', k2_scale / n, -c1[m] / (2 R2)), exact too
   float cm2[2];       // bits = 1: cm2[0] = stage-1 centroid magnitude in stage-2 units;
                       // bits = 2: cm2[0] = half the gap between the two centroid magnitudes,
                       // in stage-2 units
-  int32_t j1max, j2max;  // bits >= 3: last bucket index of each table
-  // bits >= 3 bucket tables: {threshold, count below the bucket (int bits), centroid
-  // magnitude below/above the threshold in stage-2 units} and {threshold, count below}.
-  float tab1[kTab1Max][4];
-  float tab2[kTab2Max][2];
+  // bits >= 3 bucket tables (see kTabBuckets): stage 1 {threshold in w1, count of
+  // thresholds below the bucket (int bits), -c1[count] / (2 R2), the same for count + 1};
+  // stage 2 {threshold in w2, count below}. A bucket without a threshold holds +inf
+  // (never exceeded).
+  float tab1[kTabEntries][4];
+  float tab2[kTabEntries][2];
   // Per-pair XOR masks flipping fp16 sign bits: pair m covers coordinates 2m (bit 15)
   // and 2m + 1 (bit 31).
   uint32_t xmask[512];

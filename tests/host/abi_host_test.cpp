@@ -4,10 +4,12 @@
 // checks hand to the launchers, and the attention plan. Device pointers are fake, aligned
 // addresses; the stubs never dereference them. Prints "ok" and exits 0 when every check
 // holds.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <random>
 #include <vector>
 
 #include "kvq.h"
@@ -66,6 +68,160 @@ void test_codebooks() {
   CHECK(kvq_build_codebooks(128, 2, nullptr, nullptr) == KVQ_ERR_ARG);
   for (int d : {0, 4, 7, 12, 96, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
   for (int bits : {0, 5, -1}) CHECK(kvq_build_codebooks(128, bits, nullptr, &cb) == KVQ_ERR_SHAPE);
+}
+
+// ------------------------------------------------------------------------- bucket tables
+
+// The 3- and 4-bit encoders quantize through bucket tables built on the host: a value is
+// scaled to w, the entry is read at the byte offset that the bits of v + 2^13 (stage 1,
+// 16-byte entries) or v + 2^14 (stage 2, 8-byte entries) give under a mask, for
+// v = clamp(w + 1/2, 0, 1), and the code is the entry's count plus [w > its threshold].
+// This replays those float32 steps (the same roundings: std::fma, float adds) on the tables
+// the host hands to the launch and checks (a) that the lookup equals a plain count of the
+// thresholds for every w of a dense sweep, far outside the table's range, and around every
+// threshold and bucket edge, (b) that the thresholds and the stage-2 offsets are the
+// codebook's boundaries and centroids in w units, and (c) that the whole two-stage decision
+// agrees with the float64 definition (count the boundaries y exceeds, then those its
+// residual exceeds) except within 1e-5 relative of a boundary, with an exact zero taking
+// the code below the middle boundary.
+
+uint32_t as_u32(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return u;
+}
+
+float clamp01(float v) { return v < 0.f ? 0.f : (v > 1.f ? 1.f : v); }
+
+// entry of w in a table of `stride` floats per entry (4: stage 1, 2: stage 2)
+const float* table_entry(const float* tab, int stride, float w) {
+  const float v = clamp01(w + 0.5f);
+  const float magic = stride == 4 ? 8192.0f : 16384.0f;
+  const uint32_t mask = stride == 4 ? 0x7F0u : 0x3F8u;
+  const uint32_t off = as_u32(v + magic) & mask;  // bytes
+  const int entry = static_cast<int>(off / (4u * stride));
+  CHECK(entry >= 0 && entry < kvq::kTabEntries);
+  return tab + std::min(entry, kvq::kTabEntries - 1) * stride;
+}
+
+int table_code(const float* tab, int stride, float w) {
+  const float* e = table_entry(tab, stride, w);
+  return static_cast<int>(as_u32(e[1])) + (w > e[0] ? 1 : 0);
+}
+
+// the distinct thresholds a table holds, ascending
+std::vector<float> table_thresholds(const float* tab, int stride) {
+  std::vector<float> t;
+  for (int j = 0; j < kvq::kTabEntries; ++j)
+    if (!std::isinf(tab[j * stride])) t.push_back(tab[j * stride]);
+  std::sort(t.begin(), t.end());
+  t.erase(std::unique(t.begin(), t.end()), t.end());
+  return t;
+}
+
+void check_lookup_against_count(const float* tab, int stride, const std::vector<float>& tw) {
+  std::vector<float> ws;
+  for (int i = -(1 << 16); i <= (1 << 16); ++i) ws.push_back(static_cast<float>(i) / 98304.0f);
+  for (float far : {0.75f, 1.0f, 3.0f, 50.0f, 1e30f}) {
+    ws.push_back(far);
+    ws.push_back(-far);
+  }
+  const int sub = stride == 4 ? 16 : 8;
+  for (int j = 0; j <= kvq::kTabBuckets; ++j) {  // bucket edges: half-way between grid points
+    float e = static_cast<float>((sub * j - 0.5) / (sub * kvq::kTabBuckets) - 0.5);
+    for (int k = 0; k < 4; ++k) e = std::nextafter(e, -1.0f);
+    for (int k = 0; k < 8; ++k, e = std::nextafter(e, 2.0f)) ws.push_back(e);
+  }
+  for (float t : tw) {
+    float e = t;
+    for (int k = 0; k < 4; ++k) e = std::nextafter(e, -1.0f);
+    for (int k = 0; k < 8; ++k, e = std::nextafter(e, 2.0f)) ws.push_back(e);
+  }
+  ws.push_back(0.0f);
+  int bad = 0;
+  for (float w : ws) {
+    int count = 0;
+    for (float t : tw) count += w > t ? 1 : 0;
+    bad += table_code(tab, stride, w) != count ? 1 : 0;
+  }
+  CHECK(bad == 0);
+}
+
+void test_bucket_tables() {
+  float* nr = fake<float>(0x40000);
+  for (int d : {8, 64, 128, 1024}) {
+    for (int bits : {3, 4}) {
+      kvq_codebooks cb;
+      CHECK(kvq_build_codebooks(d, bits, nullptr, &cb) == KVQ_OK);
+      kvq::g_stub = kvq::StubLog{};
+      CHECK(kvq_rvq_encode_pack(&cb, fake<uint16_t>(0x10000), 1, 1, 1, fake<uint32_t>(0x20000),
+                                fake<uint32_t>(0x30000), nr, 1, 0, nullptr) == KVQ_OK);
+      const kvq::EncodeArgs& a = kvq::g_stub.enc;
+      const float* t1 = &a.tab1[0][0];
+      const float* t2 = &a.tab2[0][0];
+      const int L = 1 << bits;
+      const std::vector<float> tv1 = table_thresholds(t1, 4), tv2 = table_thresholds(t2, 2);
+      CHECK(static_cast<int>(tv1.size()) == L - 1 && static_cast<int>(tv2.size()) == L - 1);
+      if (static_cast<int>(tv1.size()) != L - 1 || static_cast<int>(tv2.size()) != L - 1) continue;
+      CHECK(tv1[L / 2 - 1] == 0.0f && tv2[L / 2 - 1] == 0.0f);  // the middle boundary 0
+      check_lookup_against_count(t1, 4, tv1);
+      check_lookup_against_count(t2, 2, tv2);
+
+      // (b) w = t / (2R): the thresholds are the boundaries, the offsets minus the centroids
+      const double sqd = std::sqrt(static_cast<double>(d));
+      const double two_r1 = 1.0 / (sqd * a.k_scale), two_r2 = 1.0 / (sqd * a.k2_scale);
+      for (int k = 0; k < L - 1; ++k) {
+        CHECK(std::fabs(tv1[k] * two_r1 - cb.b1[k]) <= 1e-6 * two_r1);
+        CHECK(std::fabs(tv2[k] * two_r2 - cb.b2[k]) <= 1e-6 * two_r2);
+      }
+      for (int j = 0; j < kvq::kTabEntries; ++j) {
+        const int m = static_cast<int>(as_u32(t1[4 * j + 1]));
+        const int m_hi = m + (std::isinf(t1[4 * j]) ? 0 : 1);
+        CHECK(m >= 0 && m_hi < L);
+        if (m < 0 || m_hi >= L) continue;
+        CHECK(std::fabs(-t1[4 * j + 2] * two_r2 - cb.c1[m]) <= 1e-6 * two_r2);
+        CHECK(std::fabs(-t1[4 * j + 3] * two_r2 - cb.c1[m_hi]) <= 1e-6 * two_r2);
+      }
+
+      // (c) the two-stage decision for a unit-norm vector (K = k_scale): y' = y_true sqrt(d)
+      std::mt19937_64 rng(1000 + 10 * d + bits);
+      std::normal_distribution<double> gauss(0.0, cb.sigma1);
+      std::uniform_real_distribution<double> wide(-1.0, 1.0);
+      const float K = a.k_scale, K2 = a.k2_scale;  // n = 1
+      int bad = 0, near = 0;
+      for (int i = 0; i < 400000; ++i) {
+        const double y = i == 0 ? 0.0 : (i % 4 == 3 ? wide(rng) : gauss(rng));
+        const float yp = static_cast<float>(y * sqd);
+        const double yt = static_cast<double>(yp) / sqd;
+        const float w1 = std::fma(yp, K, 0.0f);
+        const float* e = table_entry(t1, 4, w1);
+        const bool gt = w1 > e[0];
+        const int c1 = static_cast<int>(as_u32(e[1])) + (gt ? 1 : 0);
+        const float w2 = std::fma(yp, K2, gt ? e[3] : e[2]);
+        const int c2 = table_code(t2, 2, w2);
+        int o1 = 0, o2 = 0;
+        for (int k = 0; k < L - 1; ++k) o1 += yt > cb.b1[k] ? 1 : 0;
+        const double r = yt - cb.c1[o1];
+        for (int k = 0; k < L - 1; ++k) o2 += r > cb.b2[k] ? 1 : 0;
+        if (i == 0) CHECK(c1 == L / 2 - 1 && c2 == o2);
+        if (c1 == o1 && c2 == o2) continue;
+        bool allowed = false;
+        if (c1 != o1) {
+          for (int k = 0; k < L - 1; ++k)
+            allowed |= std::abs(c1 - o1) == 1 &&
+                       std::fabs(yt - cb.b1[k]) <= 1e-5 * std::fmax(std::fabs(cb.b1[k]), cb.sigma1);
+        } else {
+          for (int k = 0; k < L - 1; ++k)
+            allowed |= std::abs(c2 - o2) == 1 &&
+                       std::fabs(r - cb.b2[k]) <= 1e-5 * std::fmax(std::fabs(cb.b2[k]), cb.sigma2);
+        }
+        near += allowed ? 1 : 0;
+        bad += allowed ? 0 : 1;
+      }
+      CHECK(bad == 0);
+      CHECK(near <= 2);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------ encode / decode
@@ -239,6 +395,7 @@ void test_status_text() {
 int main() {
   test_codebooks();
   test_encode_decode();
+  test_bucket_tables();
   test_qjl();
   test_attend();
   test_status_text();
