@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   __shared__ __align__(16) float ztv[NT];
   __shared__ uint32_t kx[D / 2];  // key signs as fp16 sign-bit masks, one word per coordinate pair
   __shared__ uint32_t vsg[(D + 31) / 32];  // value signs, bit c of word c / 32
-  __shared__ uint32_t cstage[S::STAGED ? kWavesPerBlock : 1][S::STAGED ? 2 * S::CSTREAM : 1];
+  constexpr bool CST = S::STAGED && !S::DIRECT3;  // codes regrouped through LDS
+  __shared__ uint32_t cstage[CST ? kWavesPerBlock : 1][CST ? 2 * S::CSTREAM : 1];
   for (int i = threadIdx.x; i < (D + 31) / 32; i += kBlockThreads) vsg[i] = a.vsign[i];
   if constexpr (P != 0) {
     fill_nibble_table<BITS>(a.ztab_k, ztk);
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kBlockThreads, attend_waves_per_eu<NQW>()) void att
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane & (L - 1);
   const int vl = lane >> LOG_L;
-  uint32_t* cs = cstage[S::STAGED ? wv : 0];
+  uint32_t* cs = cstage[CST ? wv : 0];
 
   // Unit u of this wave: (b, hkv, chunk, query group), the query group fastest, so the waves
   // of a block read the same packed keys and values.

@@ -337,11 +337,17 @@ struct CodeShape {
   static constexpr int EPW = 32 / BITS;                // codes per word
   static constexpr int NW = (D + EPW - 1) / EPW;       // words per vector per stream
   static constexpr bool STAGED = BITS == 3 && L > 1;   // 10-code words straddle lanes
+  // STAGED with 32 codes per lane: the lane's codes are bits [96 q, 96 q + 96) of the
+  // vector's stream without the words' two spare bits, which always lie in the four
+  // consecutive words from floor(96 q / 30) on; the lane loads those and takes its codes
+  // out in registers (slice3_codes)
+  static constexpr bool DIRECT3 = STAGED && C == 32;
   static constexpr bool SUB = !STAGED && L > 1 && C < EPW;  // a word holds several lanes' codes
-  // words a lane loads per stream: its own NWL consecutive words, or for STAGED words
-  // q, q + L, ... of the vector (regrouped through LDS by stage_codes), or for SUB the one
-  // word holding its codes, shifted so that they start at bit 0
-  static constexpr int NWL = STAGED ? (NW + L - 1) / L : SUB ? 1 : (L == 1 ? NW : C / EPW);
+  // words a lane loads per stream: its own NWL consecutive words, or for DIRECT3 the four
+  // words that hold its slice, or for other STAGED shapes words q, q + L, ... of the vector
+  // (regrouped through LDS by stage_codes), or for SUB the one word holding its codes,
+  // shifted so that they start at bit 0
+  static constexpr int NWL = DIRECT3 ? 4 : STAGED ? (NW + L - 1) / L : SUB ? 1 : (L == 1 ? NW : C / EPW);
   static constexpr int CSTREAM = 64 * C / 4;           // STAGED: LDS dwords per stream per wave
 };
 
@@ -350,7 +356,13 @@ template <int D, int BITS, int CM = 32>
 __device__ __forceinline__ void load_lane_words(const uint32_t* p, int64_t row, int q,
                                                 uint32_t (&w)[CodeShape<D, BITS, CM>::NWL]) {
   using S = CodeShape<D, BITS, CM>;
-  if constexpr (S::STAGED) {
+  if constexpr (S::DIRECT3) {
+    // words a .. a + 3, a = floor(96 q / 30); a + 3 is the word holding the vector's last
+    // code when q = L - 1, so every index is inside the row
+    const uint32_t* src = p + row * S::NW + (96 * q) / 30;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = src[k];
+  } else if constexpr (S::STAGED) {
 #pragma unroll
     for (int k = 0; k < S::NWL; ++k) {
       const int wi = q + S::L * k < S::NW ? q + S::L * k : S::NW - 1;
@@ -388,6 +400,26 @@ __device__ __forceinline__ void stage_codes(const uint32_t (&w)[CodeShape<D, BIT
   }
 }
 
+// DIRECT3: the lane's 96-bit slice from its four words w[0..3] (word a = floor(96 q / 30),
+// the slice starting at bit o = 96 q - 30 a of its 30 code bits): d[0..2] with code j of
+// the lane in bits [3 j, 3 j + 3) of the 96. Spare bits (30, 31) of the words are dropped.
+__device__ __forceinline__ void slice3_words(const uint32_t (&w)[4], int q, uint32_t (&d)[3]) {
+  const uint32_t o = static_cast<uint32_t>(96 * q - 30 * ((96 * q) / 30));  // 0, 6, 12, 18 or 24
+  d[0] = __builtin_amdgcn_ubfe(w[0], o, 30u - o) | (w[1] << (30u - o));
+  d[1] = __builtin_amdgcn_ubfe(w[1], o + 2u, 28u - o) | (w[2] << (28u - o));
+  d[2] = __builtin_amdgcn_ubfe(w[2], o + 4u, 26u - o) | (w[3] << (26u - o));
+}
+
+// Code j (0 <= j < 32) of a DIRECT3 slice; codes 10 and 21 straddle dwords.
+template <int J>
+__device__ __forceinline__ uint32_t slice3_code(const uint32_t (&d)[3]) {
+  if constexpr (J < 10) return __builtin_amdgcn_ubfe(d[0], 3u * J, 3u);
+  else if constexpr (J == 10) return __builtin_amdgcn_alignbit(d[1], d[0], 30) & 7u;
+  else if constexpr (J < 21) return __builtin_amdgcn_ubfe(d[1], 3u * J - 32u, 3u);
+  else if constexpr (J == 21) return __builtin_amdgcn_alignbit(d[2], d[1], 31) & 7u;
+  else return __builtin_amdgcn_ubfe(d[2], 3u * J - 64u, 3u);
+}
+
 // Code of local coordinate j (0 <= j < C) of this lane, from its own words (not STAGED).
 template <int D, int BITS, int CM = 32>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[CodeShape<D, BITS, CM>::NWL], int j) {
@@ -397,7 +429,7 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[CodeShape<D, BIT
 
 // Dequantized rotated-domain coordinates z[j] = table[(i1 << BITS) | i2] of this lane
 // (i2 = 0 when TWO is false). `zt` is the LDS table, `cs` the wave's LDS staging area for
-// STAGED codes (two streams of CSTREAM dwords; unused otherwise).
+// STAGED codes other than DIRECT3 (two streams of CSTREAM dwords; unused otherwise).
 template <int D, int BITS, bool TWO, int CM = 32>
 __device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BITS, CM>::NWL],
                                            const uint32_t (&w2)[CodeShape<D, BITS, CM>::NWL], const float* zt,
@@ -412,6 +444,16 @@ __device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BIT
       const uint32_t i2 = TWO ? code_at<D, BITS, CM>(w2, j) : 0u;
       z[j] = zt[(i1 << BITS) | i2];
     }
+  } else if constexpr (S::DIRECT3) {
+    uint32_t d1[3], d2[3] = {0u, 0u, 0u};
+    slice3_words(w1, q, d1);
+    if constexpr (TWO) slice3_words(w2, q, d2);
+    static_for<0, 32>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      const uint32_t i1 = slice3_code<j>(d1);
+      const uint32_t i2 = TWO ? slice3_code<j>(d2) : 0u;
+      z[j] = zt[(i1 << 3) | i2];
+    });
   } else {
     stage_codes<D, BITS, CM>(w1, cs, vl, q);
     if constexpr (TWO) stage_codes<D, BITS, CM>(w2, cs + S::CSTREAM, vl, q);

@@ -379,7 +379,8 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ uint4 smask[D / 8];
   __shared__ float zt[NZ];
-  __shared__ uint32_t cstage[S::STAGED ? kWavesPerBlock : 1][S::STAGED ? STAGES * S::CSTREAM : 1];
+  constexpr bool CST = S::STAGED && !S::DIRECT3;  // codes regrouped through LDS
+  __shared__ uint32_t cstage[CST ? kWavesPerBlock : 1][CST ? STAGES * S::CSTREAM : 1];
   for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
   for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   __syncthreads();
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   const int q = lane & (L - 1);
   const int vl = lane >> LOG_L;
   uint4* buf = stage[wv];
-  uint32_t* cs = cstage[S::STAGED ? wv : 0];
+  uint32_t* cs = cstage[CST ? wv : 0];
   const int n_tiles = static_cast<int>((a.n_vec + VW - 1) / VW);
   const int stride = static_cast<int>(gridDim.x) * kWavesPerBlock;
   const bool negated = (__builtin_popcount(q) & 1) != 0;
