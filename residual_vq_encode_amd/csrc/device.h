@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <stdint.h>
 
 #include "params.h"
@@ -472,15 +474,63 @@ __device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BIT
   }
 }
 
+// 1- and 2-bit codes: z after the first log2(G) butterfly stages, straight from a group
+// table. A nibble of a stream word holds the codes of G = 4 / BITS consecutive coordinates;
+// the two streams' nibbles n1 | n2 << 4 index 256 entries of G floats, the float32
+// operations of the table lookups z = c1[i1] + c2[i2] followed by lane_stages' first stages
+// (BITS = 2: {z0 + z1, z0 - z1}; BITS = 1: the two stages over four coordinates). The even
+// and the odd nibbles of a word take their indices from the bytes of two interleaved words.
+template <int BITS>
+using GroupEntry = typename std::conditional<BITS == 2, float2, float4>::type;
+
+template <int D, int BITS, bool TWO, int CM = 32>
+__device__ __forceinline__ void codes_to_groups(const uint32_t (&w1)[CodeShape<D, BITS, CM>::NWL],
+                                                const uint32_t (&w2)[CodeShape<D, BITS, CM>::NWL],
+                                                const GroupEntry<BITS>* gt, float (&z)[Layout<D, CM>::C]) {
+  using S = CodeShape<D, BITS, CM>;
+  constexpr int C = S::C, G = 4 / BITS;
+  static_assert(BITS == 1 || BITS == 2, "four code bits per nibble");
+  static_assert(!S::STAGED && !S::SUB, "a lane's own words");
+#pragma unroll
+  for (int k = 0; k < S::NWL; ++k) {
+    const uint32_t a = w1[k], b = TWO ? w2[k] : 0u;
+    const uint32_t ev = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);  // nibbles 0, 2, 4, 6
+    const uint32_t od = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);  // nibbles 1, 3, 5, 7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = S::EPW * k + 2 * G * i;  // first coordinate of nibble 2i of word k
+      if (j < C) {
+        const GroupEntry<BITS> e = gt[(ev >> (8 * i)) & 0xFFu];
+        z[j] = e.x;
+        z[j + 1] = e.y;
+        if constexpr (G == 4) {
+          z[j + 2] = e.z;
+          z[j + 3] = e.w;
+        }
+      }
+      if (j + G < C) {
+        const GroupEntry<BITS> f = gt[(od >> (8 * i)) & 0xFFu];
+        z[j + G] = f.x;
+        z[j + G + 1] = f.y;
+        if constexpr (G == 4) {
+          z[j + G + 2] = f.z;
+          z[j + G + 3] = f.w;
+        }
+      }
+    }
+  }
+}
+
 // The inverse rotation of this lane's slice and the conversion to fp16 pairs:
 // o = RN16(K * (H z)) per coordinate pair, H applied in registers then across the L lanes
 // of the vector. K must carry the lane's sign (-1)^popcount(q) (see cross_stage); the
-// caller applies the final diag(s) to the fp16 pairs (an XOR of sign bits).
-template <int D, int CM = 32>
+// caller applies the final diag(s) to the fp16 pairs (an XOR of sign bits). H0 > 1: z has
+// had the in-register stages below H0 already (codes_to_groups).
+template <int D, int CM = 32, int H0 = 1>
 __device__ __forceinline__ void unrotate_f16(float (&z)[(Layout<D, CM>::C)], float K, int q,
                                              uint32_t (&o)[(Layout<D, CM>::C) / 2]) {
   constexpr int C = Layout<D, CM>::C;
-  lane_stages<C, 1>(z);
+  lane_stages<C, H0>(z);
   cross_stages<C, Layout<D, CM>::LOG_L>(z, q);
 #pragma unroll
   for (int m = 0; m < C / 2; ++m) {

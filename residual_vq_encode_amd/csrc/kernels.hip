@@ -375,13 +375,36 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   constexpr int NWL = S::NWL;
   constexpr int NZ = 1 << (2 * BITS);
   constexpr bool TWO = STAGES == 2;
+  // 1- and 2-bit codes: dequantize groups of GS = 4 / BITS coordinates through a 256-entry
+  // table that also does the first log2(GS) butterfly stages (codes_to_groups)
+  constexpr bool GROUPS = BITS <= 2;
+  constexpr int GS = 4 / BITS;
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ uint4 smask[D / 8];
   __shared__ float zt[NZ];
+  __shared__ GroupEntry<BITS <= 2 ? BITS : 2> gt[GROUPS ? 256 : 1];
   constexpr bool CST = S::STAGED && !S::DIRECT3;  // codes regrouped through LDS
   __shared__ uint32_t cstage[CST ? kWavesPerBlock : 1][CST ? STAGES * S::CSTREAM : 1];
   for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
+  if constexpr (GROUPS) {
+    // entry n1 | n2 << 4: coordinate t of the group has codes (i1, i2) = bits t of n1 and
+    // of n2 (BITS = 1), or bit pairs t (BITS = 2); the same float32 sums and differences as
+    // the first stages of lane_stages
+    for (int i = threadIdx.x; i < 256; i += kBlockThreads) {
+      constexpr uint32_t M = (1u << BITS) - 1u;
+      float zz[GS];
+#pragma unroll
+      for (int t = 0; t < GS; ++t)
+        zz[t] = a.ztab[(((i >> (BITS * t)) & M) << BITS) | ((i >> (4 + BITS * t)) & M)];
+      if constexpr (GS == 2) {
+        gt[i] = make_float2(zz[0] + zz[1], zz[0] - zz[1]);
+      } else {
+        const float s0 = zz[0] + zz[1], d0 = zz[0] - zz[1], s1 = zz[2] + zz[3], d1 = zz[2] - zz[3];
+        gt[i] = make_float4(s0 + s1, d0 + d1, s0 - s1, d0 - d1);
+      }
+    }
+  }
   for (int i = threadIdx.x; i < D / 2; i += kBlockThreads) reinterpret_cast<uint32_t*>(smask)[i] = a.xmask[i];
   __syncthreads();
 
@@ -439,14 +462,15 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
 
     // 1. Codes of this lane's C coordinates -> z = c1[i1] + c2[i2] (or c1[i1]).
     float z[C];
-    codes_to_z<D, BITS, TWO>(w1, w2, zt, cs, lane, vl, q, z);
+    if constexpr (GROUPS) codes_to_groups<D, BITS, TWO>(w1, w2, gt, z);
+    else codes_to_z<D, BITS, TWO>(w1, w2, zt, cs, lane, vl, q, z);
 
     // 2. Inverse rotation: H z (H symmetric), scaled by n / sqrt(D) (carrying the lane's
     //    sign), then the final sign flip as an exact XOR of fp16 sign bits.
     float K = nrm * a.inv_sqrt_d;
     if (negated) K = -K;
     uint32_t o[C / 2];
-    unrotate_f16<D>(z, K, q, o);
+    unrotate_f16<D, 32, GROUPS ? GS : 1>(z, K, q, o);
 
     // 3. Transpose through LDS into the chunk order of the (contiguous) output tile, for
     //    coalesced 16-byte stores.
