@@ -439,7 +439,22 @@ __device__ __forceinline__ void codes_to_z(const uint32_t (&w1)[CodeShape<D, BIT
   using S = CodeShape<D, BITS, CM>;
   constexpr int C = S::C;
   constexpr uint32_t MASK = (1u << BITS) - 1u;
-  if constexpr (!S::STAGED) {
+  if constexpr (BITS == 4 && !S::SUB) {
+    // a word holds 8 codes, one per nibble: the table index (i1 << 4) | i2 of coordinates
+    // 0, 2, 4, 6 of a word are the bytes of one interleave of the two streams' words, those
+    // of coordinates 1, 3, 5, 7 the bytes of another
+#pragma unroll
+    for (int k = 0; k < S::NWL; ++k) {
+      const uint32_t a = w1[k], b = TWO ? w2[k] : 0u;
+      const uint32_t ev = ((a << 4) & 0xF0F0F0F0u) | (b & 0x0F0F0F0Fu);
+      const uint32_t od = (a & 0xF0F0F0F0u) | ((b >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (8 * k + 2 * i < C) z[8 * k + 2 * i] = zt[(ev >> (8 * i)) & 0xFFu];
+        if (8 * k + 2 * i + 1 < C) z[8 * k + 2 * i + 1] = zt[(od >> (8 * i)) & 0xFFu];
+      }
+    }
+  } else if constexpr (!S::STAGED) {
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const uint32_t i1 = code_at<D, BITS, CM>(w1, j);
