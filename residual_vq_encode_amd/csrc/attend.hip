@@ -836,9 +836,29 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine(const AttendAr
   const float* wq = a.ws + qv * a.n_splits * (D + 4);
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
 
-  // pass 1: M, the weights, S
+  // The records' coordinate quads of the first CPF chunks of this thread are loaded first:
+  // they do not depend on pass 1, so their latency overlaps it.
+  constexpr int CPF = 16;
+  const int qd = t % Q4, grp = t / Q4;
+  float4 pre[CPF];
+#pragma unroll
+  for (int r = 0; r < CPF; ++r) {
+    const int sp = grp + r * NG;
+    pre[r] = sp < a.n_splits ? reinterpret_cast<const float4*>(wq + sp * (D + 4) + 4 + c0)[qd]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  // pass 1: M, the weights, S; each chunk header {m, l} is read once, as one 8-byte load,
+  // and kept in registers (a thread owns at most kMaxSplits / kCombineThreads chunks)
+  constexpr int HPT = kMaxSplits / kCombineThreads;
+  float2 ml[HPT];
   float M = -FLT_MAX;
-  for (int sp = t; sp < a.n_splits; sp += kCombineThreads) M = __builtin_fmaxf(M, wq[sp * (D + 4)]);
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int sp = t + k * kCombineThreads;
+    ml[k] = sp < a.n_splits ? *reinterpret_cast<const float2*>(wq + sp * (D + 4)) : make_float2(-FLT_MAX, 0.f);
+    M = __builtin_fmaxf(M, ml[k].x);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) red[0][wv] = M;
@@ -846,10 +866,14 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine(const AttendAr
 #pragma unroll
   for (int k = 0; k < kCombineThreads / 64; ++k) M = __builtin_fmaxf(M, red[0][k]);
   float S = 0.f;
-  for (int sp = t; sp < a.n_splits; sp += kCombineThreads) {
-    const float f = exp2_fast(wq[sp * (D + 4)] - M);
-    fs[sp] = f;
-    S += f * wq[sp * (D + 4) + 1];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int sp = t + k * kCombineThreads;
+    if (sp < a.n_splits) {
+      const float f = exp2_fast(ml[k].x - M);
+      fs[sp] = f;
+      S += f * ml[k].y;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
@@ -860,10 +884,18 @@ __global__ __launch_bounds__(kCombineThreads) void attend_combine(const AttendAr
   for (int k = 0; k < kCombineThreads / 64; ++k) S += red[1][k];
 
   // pass 2: sum_s f_s u_s over this block's coordinates
-  const int qd = t % Q4, grp = t / Q4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int r = 0; r < CPF; ++r) {
+    const int sp = grp + r * NG;
+    const float f = sp < a.n_splits ? fs[sp] : 0.f;
+    acc.x = __builtin_fmaf(f, pre[r].x, acc.x);
+    acc.y = __builtin_fmaf(f, pre[r].y, acc.y);
+    acc.z = __builtin_fmaf(f, pre[r].z, acc.z);
+    acc.w = __builtin_fmaf(f, pre[r].w, acc.w);
+  }
 #pragma unroll 8
-  for (int sp = grp; sp < a.n_splits; sp += NG) {
+  for (int sp = grp + CPF * NG; sp < a.n_splits; sp += NG) {
     const float f = fs[sp];
     const float4 v = reinterpret_cast<const float4*>(wq + sp * (D + 4) + 4 + c0)[qd];
     acc.x = __builtin_fmaf(f, v.x, acc.x);
