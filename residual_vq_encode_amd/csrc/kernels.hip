@@ -87,6 +87,14 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
       t2s[i] = in ? make_float2(a.tab2[i][0], a.tab2[i][1]) : make_float2(__builtin_inff(), 0.f);
     }
   }
+  // 3-bit codes into a contiguous cache: a tile's words are one run of VW * NW words per
+  // stream (16-byte aligned when that count is a multiple of 4). The lanes' own words are 3
+  // or 4 scattered dwords each, so they are dropped into LDS and the wave writes the run
+  // back with 16-byte stores.
+  constexpr int TW = VW * NW;
+  constexpr bool RUN3 = STAGED && CONTIG && TW % 4 == 0;
+  constexpr int NSTREAM = TWO ? 2 : 1;
+  __shared__ uint32_t pk[RUN3 ? kWavesPerBlock : 1][RUN3 ? NSTREAM * TW : 1];
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -126,6 +134,54 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
   uint32_t w1[NWL], w2[NWL];
   float n_prev = 0.f;
   int64_t row_prev = -1;  // -1: nothing to store (first tile, or a lane past the last vector)
+  int64_t v0_prev = -1;   // RUN3: the previous tile's first vector (-1: none) and its count
+  int nv_prev = 0;
+  // Stores the previous tile's norms and words.
+  auto store_prev = [&]() {
+    if (row_prev >= 0 && q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
+    if constexpr (RUN3) {
+      if (v0_prev < 0) return;  // wave-uniform
+      uint32_t* pw = pk[wv];
+      if (row_prev >= 0) {
+        const int base = vl * NW + s_word;
+#pragma unroll
+        for (int k = 0; k < NWL; ++k) {
+          if (k < 3 || s_off == 0) {
+            pw[base + k] = w1[k];
+            if constexpr (TWO) pw[TW + base + k] = w2[k];
+          }
+        }
+      }
+      wave_lds_fence();
+      const int valid = nv_prev * NW;  // words of the run that belong to vectors
+      static_assert(TW / 4 <= 64, "one 16-byte chunk per lane");
+#pragma unroll
+      for (int st = 0; st < NSTREAM; ++st) {
+        uint32_t* dst = (st == 0 ? a.p1 : a.p2) + v0_prev * NW;
+        if (4 * lane + 4 <= valid) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(pw + st * TW + 4 * lane);
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst) + lane);
+        } else if (4 * lane < valid) {
+          for (int e = 4 * lane; e < valid; ++e) __builtin_nontemporal_store(pw[st * TW + e], dst + e);
+        }
+      }
+      wave_lds_fence();  // the reads above complete before the next tile's words land
+    } else {
+      if (row_prev < 0) return;
+      if constexpr (STAGED) {
+#pragma unroll
+        for (int k = 0; k < NWL; ++k) {
+          if (k < 3 || s_off == 0) {
+            __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + s_word + k);
+            if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + s_word + k);
+          }
+        }
+      } else {
+        store_words<NWL>(a.p1 + row_prev * NW + q * NWL, w1);
+        if constexpr (TWO) store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
+      }
+    }
+  };
   for (; tile < n_tiles; tile += stride) {
     const int64_t v0 = static_cast<int64_t>(tile) * VW;
     const int nv = static_cast<int>(a.n_vec - v0 < VW ? a.n_vec - v0 : VW);
@@ -165,21 +221,7 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     // 2. Store the previous tile, then start loading the next tile into the buffer this
     //    tile has just left. Lanes hold consecutive slices of consecutive vectors, so a
     //    wave writes contiguous runs.
-    if (row_prev >= 0) {
-      if (q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
-      if constexpr (STAGED) {
-#pragma unroll
-        for (int k = 0; k < NWL; ++k) {
-          if (k < 3 || s_off == 0) {
-            __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + s_word + k);
-            if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + s_word + k);
-          }
-        }
-      } else {
-        store_words<NWL>(a.p1 + row_prev * NW + q * NWL, w1);
-        if constexpr (TWO) store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
-      }
-    }
+    store_prev();
     {
       const int nt = tile + stride;
       if (nt < n_tiles) {
@@ -345,22 +387,10 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
       const int64_t r = cache_row<CONTIG>(a.map, v0, vl);
       row_prev = (vl < nv) ? r : -1;
     }
+    v0_prev = v0;
+    nv_prev = nv;
   }
-  if (row_prev >= 0) {
-    if (q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
-    if constexpr (STAGED) {
-#pragma unroll
-      for (int k = 0; k < NWL; ++k) {
-        if (k < 3 || s_off == 0) {
-          __builtin_nontemporal_store(w1[k], a.p1 + row_prev * NW + s_word + k);
-          if constexpr (TWO) __builtin_nontemporal_store(w2[k], a.p2 + row_prev * NW + s_word + k);
-        }
-      }
-    } else {
-      store_words<NWL>(a.p1 + row_prev * NW + q * NWL, w1);
-      if constexpr (TWO) store_words<NWL>(a.p2 + row_prev * NW + q * NWL, w2);
-    }
-  }
+  store_prev();
 }
 
 // ------------------------------------------------------------------------------ decode
