@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
   int nv_prev = 0;
   // Stores the previous tile's norms and words.
   auto store_prev = [&]() {
-    if (row_prev >= 0 && q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
     if constexpr (RUN3) {
+      if (row_prev >= 0 && q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
       if (v0_prev < 0) return;  // wave-uniform
       uint32_t* pw = pk[wv];
       if (row_prev >= 0) {
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
         }
       }
       wave_lds_fence();  // the reads above complete before the next tile's words land
-    } else {
-      if (row_prev < 0) return;
+    } else if (row_prev >= 0) {
+      if (q == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
       if constexpr (STAGED) {
 #pragma unroll
         for (int k = 0; k < NWL; ++k) {
