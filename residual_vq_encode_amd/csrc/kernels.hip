@@ -244,12 +244,12 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     const float n = __builtin_amdgcn_sqrtf(ss);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 4. Quantize both stages and pack. K maps the raw transform to the stage-1 unit with
-    //    the sign flipped: NX = fma(y', -K, +0) = -(y_true * unit1) (K carries the lane's
-    //    sign). Adding +0 turns an exact zero into +0, so sign(NX) is exactly [y_true > 0]
-    //    (the count semantics at the middle boundary 0). A zero vector gets K = 0, so
-    //    y_true = 0. The stage-2 value X2 = (|y_true| - cm) * unit2 is formed from y'
-    //    directly (K2 = |K| * r12), one rounding.
+    // 4. Quantize both stages and pack. BITS <= 2: K maps the raw transform to the stage-1
+    //    unit with the sign flipped: NX = fma(y', -K, +0) = -(y_true * unit1) (K carries the
+    //    lane's sign). Adding +0 turns an exact zero into +0, so sign(NX) is exactly
+    //    [y_true > 0] (the count semantics at the middle boundary 0). A zero vector gets
+    //    K = 0, so y_true = 0. The stage-2 value X2 = (|y_true| - cm) * unit2 is formed from
+    //    y' directly (K2 = |K| * r12), one rounding.
     //    BITS >= 3 compare w1 = fma(y', K, +0) = y_true / (2 R1) and
     //    w2 = fma(y', K2s, -c1[m] / (2 R2)) = (y_true - c1[m]) / (2 R2) (K2s carries the lane's
     //    sign as K does) with thresholds in the same units: an exact zero gives w1 = +0, which
@@ -412,11 +412,12 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
 
   __shared__ uint4 stage[kWavesPerBlock][64 * CH];
   __shared__ uint4 smask[D / 8];
-  __shared__ float zt[NZ];
+  __shared__ float zt[GROUPS ? 1 : NZ];  // per-coordinate table (b >= 3)
   __shared__ GroupEntry<BITS <= 2 ? BITS : 2> gt[GROUPS ? 256 : 1];
   constexpr bool CST = S::STAGED && !S::DIRECT3;  // codes regrouped through LDS
   __shared__ uint32_t cstage[CST ? kWavesPerBlock : 1][CST ? STAGES * S::CSTREAM : 1];
-  for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
+  if constexpr (!GROUPS)
+    for (int i = threadIdx.x; i < NZ; i += kBlockThreads) zt[i] = a.ztab[i];
   if constexpr (GROUPS) {
     // entry n1 | n2 << 4: coordinate t of the group has codes (i1, i2) = bits t of n1 and
     // of n2 (BITS = 1), or bit pairs t (BITS = 2); the same float32 sums and differences as
