@@ -129,7 +129,7 @@ float as_float(int32_t v) {
 kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
   const int d = cb->d, bits = cb->bits;
   const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
-  std::memset(a->xmask, 0, sizeof(a->xmask));
+  std::memset(a->wpair, 0, sizeof(a->wpair));
   std::memset(a->tab1, 0, sizeof(a->tab1));
   std::memset(a->tab2, 0, sizeof(a->tab2));
   a->k2_scale = 0.f;
@@ -164,7 +164,8 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
     }
   }
   for (int m = 0; m < d / 2; ++m)
-    a->xmask[m] = (sign_of(cb, 2 * m) < 0 ? 0x8000u : 0u) | (sign_of(cb, 2 * m + 1) < 0 ? 0x80000000u : 0u);
+    a->wpair[m] =
+        kvq::kOnePair ^ ((sign_of(cb, 2 * m) < 0 ? 0x8000u : 0u) | (sign_of(cb, 2 * m + 1) < 0 ? 0x80000000u : 0u));
   return KVQ_OK;
 }
 

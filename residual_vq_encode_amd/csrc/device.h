@@ -91,7 +91,7 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // instructions but cannot know about for inline asm. (Inside the block the partial sums are
 // read only as the addend of the same opcode, which needs none.) Written as asm because the
 // compiler otherwise picks the accumulating v_dot2c and spends a move per product.
-constexpr uint32_t kPP = 0x3C003C00u;  // fp16 (+1, +1)
+constexpr uint32_t kPP = kOnePair;  // fp16 (+1, +1)
 
 __device__ __forceinline__ void dot2_stages8(const uint32_t (&xh)[4], const uint32_t (&w)[4], float (&o)[8]) {
   float s0, d0, s1, d1;

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
   // fp16 weights (s_2p, s_2p+1) of this lane's C/2 coordinate pairs: the rotation's signs
   uint32_t wt[C / 2];
 #pragma unroll
-  for (int p = 0; p < C / 2; ++p) wt[p] = kPP ^ a.xmask[q * (C / 2) + p];
+  for (int p = 0; p < C / 2; ++p) wt[p] = a.wpair[q * (C / 2) + p];
 
   int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
   if (tile < n_tiles) {

@@ -21,6 +21,8 @@ constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
 // 1 / (kTabSub * kTabBuckets) in [2^e, 2^(e+1)): masked, they are the entry's byte offset.
 // Stage 1 entries are 16 bytes (kTabSub = 16, e = 13), stage 2 entries 8 bytes (kTabSub = 8,
 // e = 14).
+constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 1.0 values
+
 constexpr int kTabBuckets = 64;
 constexpr int kTabEntries = kTabBuckets + 1;
 
@@ -55,9 +57,11 @@ struct EncodeArgs {
   // (never exceeded).
   float tab1[kTabEntries][4];
   float tab2[kTabEntries][2];
-  // Per-pair XOR masks flipping fp16 sign bits: pair m covers coordinates 2m (bit 15)
-  // and 2m + 1 (bit 31).
-  uint32_t xmask[512];
+  // Per-pair fp16 weights (s_2m, s_2m+1) of the first butterfly stages: the pair (1, 1)
+  // with the sign bit of each coordinate the rotation negates set (bit 15: coordinate 2m,
+  // bit 31: 2m + 1). The host folds the signs into the pair so the kernel's prologue only
+  // loads them; each wave sees only a few tiles, so its setup counts.
+  uint32_t wpair[512];
 };
 
 struct DecodeArgs {
