@@ -35,13 +35,43 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// One stage's tables as the kernels rely on them: 2^bits finite centroids, strictly
+// ascending and exactly antisymmetric (c[k] == -c[L-1-k]), and boundaries that are the
+// float32 roundings of the midpoints of neighbouring centroids, computed in double ("rvq" tag
+// page, "What 'quantize' means here, precisely": counting boundary crossings picks the
+// nearest centroid only when the boundaries are those midpoints). Antisymmetry then makes
+// the middle boundary +0.0, which the kernels' sign-bit quantizers (bits <= 2) assume, and
+// the 3- and 4-bit bucket tables are derived from these boundaries.
+bool stage_tables_ok(const float* c, const float* b, int bits) {
+  const int L = 1 << bits;
+  for (int k = 0; k < L; ++k) {
+    if (!std::isfinite(c[k]) || c[k] != -c[L - 1 - k]) return false;
+    if (k + 1 < L && !(c[k] < c[k + 1])) return false;
+  }
+  for (int k = 0; k + 1 < L; ++k) {
+    const float mid = static_cast<float>((static_cast<double>(c[k]) + static_cast<double>(c[k + 1])) * 0.5);
+    uint32_t got, want;
+    std::memcpy(&got, &b[k], 4);
+    std::memcpy(&want, &mid, 4);
+    if (got != want) return false;  // bit equality: the middle boundary must be +0.0, not -0.0
+  }
+  return true;
+}
+
 kvq_status check_codebooks(const kvq_codebooks* cb) {
   if (cb == nullptr) return KVQ_ERR_ARG;
   if (cb->d < KVQ_MIN_D || cb->d > KVQ_MAX_D || !is_pow2(cb->d)) return KVQ_ERR_SHAPE;
   if (cb->bits < 1 || cb->bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
   const int epw = 32 / cb->bits;
   if (cb->elems_per_word != epw || cb->n_words != (cb->d + epw - 1) / epw) return KVQ_ERR_ARG;
+  if (!stage_tables_ok(cb->c1, cb->b1, cb->bits) || !stage_tables_ok(cb->c2, cb->b2, cb->bits)) return KVQ_ERR_ARG;
   return KVQ_OK;
+}
+
+// The codec kernels walk their tiles with 32-bit indices: a launch may hold at most INT_MAX.
+kvq_status check_tiles(int64_t n_vec, int64_t vectors_per_tile) {
+  return (n_vec + vectors_per_tile - 1) / vectors_per_tile > std::numeric_limits<int32_t>::max() ? KVQ_ERR_RANGE
+                                                                                                 : KVQ_OK;
 }
 
 int sign_of(const kvq_codebooks* cb, int j) { return ((cb->sign_bits[j >> 5] >> (j & 31)) & 1u) ? -1 : 1; }
@@ -200,6 +230,8 @@ kvq_status encode_pack(const kvq_codebooks* cb, int stages, const uint16_t* x, i
     return KVQ_ERR_ARG;
   if (!aligned(x, 16) || !aligned(packed1, 16) || (stages == 2 && !aligned(packed2, 16)) || !aligned(norms, 4))
     return KVQ_ERR_ALIGN;
+  st = check_tiles(n_vec, kvq::encode_tile_vectors(cb->d, cb->bits));
+  if (st != KVQ_OK) return st;
 
   EncodeArgs a;
   a.x = x;
@@ -226,6 +258,8 @@ kvq_status unpack_decode(const kvq_codebooks* cb, int stages, const uint32_t* pa
   if (packed1 == nullptr || (stages == 2 && packed2 == nullptr) || x_out == nullptr) return KVQ_ERR_ARG;
   if (!aligned(x_out, 16) || !aligned(packed1, 16) || (stages == 2 && !aligned(packed2, 16)) || !aligned(norms, 4))
     return KVQ_ERR_ALIGN;
+  st = check_tiles(n_vec, kvq::decode_tile_vectors(cb->d));
+  if (st != KVQ_OK) return st;
 
   DecodeArgs a;
   a.p1 = packed1;

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <random>
 #include <vector>
 
@@ -288,6 +289,94 @@ void test_encode_decode() {
   CHECK(kvq::g_stub.stages == 1);
 }
 
+// Codebook structs that break what the kernels assume (ascending, exactly antisymmetric
+// tables whose boundaries are the float32 midpoints of neighbouring centroids, so the middle
+// boundary is +0.0) are rejected with KVQ_ERR_ARG before anything is launched, at every bit
+// width and by every entry point that takes them.
+void test_tampered_codebooks() {
+  uint16_t* x = fake<uint16_t>(0x10000);
+  uint32_t* p1 = fake<uint32_t>(0x20000);
+  uint32_t* p2 = fake<uint32_t>(0x30000);
+  float* nr = fake<float>(0x40000);
+  for (int bits = 1; bits <= 4; ++bits) {
+    kvq_codebooks cb;
+    CHECK(kvq_build_codebooks(128, bits, nullptr, &cb) == KVQ_OK);
+    const int L = 1 << bits;
+    auto rejected = [&](const kvq_codebooks& bad) {
+      kvq::g_stub = kvq::StubLog{};
+      bool ok = kvq_rvq_encode_pack(&bad, x, 1, 2, 8, p1, p2, nr, 8, 0, nullptr) == KVQ_ERR_ARG &&
+                kvq_rvq_unpack_decode(&bad, p1, p2, nr, 1, 2, 8, 0, 8, x, nullptr) == KVQ_ERR_ARG &&
+                kvq_mse_encode_pack(&bad, x, 1, 2, 8, p1, nr, 8, 0, nullptr) == KVQ_ERR_ARG;
+      return ok && kvq::g_stub.encode_calls == 0 && kvq::g_stub.decode_calls == 0;
+    };
+    kvq_codebooks bad = cb;
+    bad.b1[L / 2 - 1] = -0.0f;  // middle boundary -0
+    CHECK(rejected(bad));
+    bad = cb;
+    bad.b2[L / 2 - 1] = -0.0f;
+    CHECK(rejected(bad));
+    bad = cb;
+    bad.c1[L - 1] = std::nextafter(cb.c1[L - 1], 1.0f);  // breaks antisymmetry (and the last midpoint)
+    CHECK(rejected(bad));
+    bad = cb;
+    bad.c2[0] = std::nextafter(cb.c2[0], -1.0f);
+    CHECK(rejected(bad));
+    bad = cb;
+    bad.b1[0] = std::nextafter(cb.b1[0], -1.0f);  // a boundary one ulp off its midpoint
+    CHECK(rejected(bad));
+    bad = cb;
+    bad.b2[L - 2] = std::nextafter(cb.b2[L - 2], 1.0f);
+    CHECK(rejected(bad));
+    bad = cb;  // both tables scaled together: still antisymmetric, still midpoints; accepted
+    for (int k = 0; k < L; ++k) bad.c1[k] *= 2.0f;
+    for (int k = 0; k + 1 < L; ++k) bad.b1[k] *= 2.0f;
+    CHECK(kvq_rvq_encode_pack(&bad, x, 1, 2, 8, p1, p2, nr, 8, 0, nullptr) == KVQ_OK);
+    bad = cb;
+    for (int k = 0; k < L; ++k) std::swap(bad.c1[k], bad.c1[L - 1 - k]);  // descending
+    for (int k = 0; k + 1 < L; ++k) bad.b1[k] = -bad.b1[k];
+    if (bits > 1) {
+      for (int k = 0; k < (L - 1) / 2; ++k) std::swap(bad.b1[k], bad.b1[L - 2 - k]);
+      CHECK(rejected(bad));
+    }
+    bad = cb;
+    bad.c1[0] = -std::numeric_limits<float>::infinity();
+    bad.c1[L - 1] = std::numeric_limits<float>::infinity();
+    CHECK(rejected(bad));
+  }
+  // the attention takes the same checks
+  kvq_codebooks ck, cv;
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &ck) == KVQ_OK);
+  cv = ck;
+  cv.b1[1] = -0.0f;
+  int64_t need = 0;
+  CHECK(kvq_rvq_attend_workspace_size(128, 2, 1, 32, 1, 8, 4096, &need) == KVQ_OK);
+  CHECK(kvq_rvq_attend(&ck, &cv, x, 1, 32, 1, 8, p1, p2, nr, p1, p2, nr, 4096, 4096, 0.1f,
+                       fake<void>(0x50000), need, x, nullptr) == KVQ_ERR_ARG);
+}
+
+// The kernels index their tiles with 32-bit integers: a launch needing more than INT_MAX
+// tiles is refused with KVQ_ERR_RANGE on the host (at d = 1024 the butterfly kernels hold 2
+// vectors per tile; at d = 128 the matrix-core encode and the decode hold 16).
+void test_tile_limit() {
+  uint16_t* x = fake<uint16_t>(0x10000);
+  uint32_t* p1 = fake<uint32_t>(0x20000);
+  uint32_t* p2 = fake<uint32_t>(0x30000);
+  float* nr = fake<float>(0x40000);
+  const int64_t imax = std::numeric_limits<int32_t>::max();
+  kvq_codebooks cb;
+  CHECK(kvq_build_codebooks(1024, 2, nullptr, &cb) == KVQ_OK);
+  kvq::g_stub = kvq::StubLog{};
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 2 * imax, p1, p2, nr, 2 * imax, 0, nullptr) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 2 * imax + 1, p1, p2, nr, 2 * imax + 1, 0, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 1, 1, 2 * imax, 0, 2 * imax, x, nullptr) == KVQ_OK);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 1, 1, 2 * imax + 2, 0, 2 * imax + 2, x, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq::g_stub.encode_calls == 1 && kvq::g_stub.decode_calls == 1);
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &cb) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax, p1, p2, nr, 16 * imax, 0, nullptr) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax + 1, p1, p2, nr, 16 * imax + 1, 0, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 1, 1, 16 * imax + 1, 0, 16 * imax + 1, x, nullptr) == KVQ_ERR_RANGE);
+}
+
 // ------------------------------------------------------------------------------ QJL
 
 void test_qjl() {
@@ -395,6 +484,8 @@ void test_status_text() {
 int main() {
   test_codebooks();
   test_encode_decode();
+  test_tampered_codebooks();
+  test_tile_limit();
   test_bucket_tables();
   test_qjl();
   test_attend();
