@@ -53,6 +53,81 @@ constexpr int encode_waves_per_eu() {
   return (!CONTIG && BITS >= 3) ? 3 : kEncodeWavesPerEU;
 }
 
+// ------------------------------------------------------------------------------ quantizers
+
+// Codes of y[JLO..JHI) for both stages, LSB-first with code JLO in bits [0, BITS) (as one
+// packed word holds them). y is the raw transform H diag(s) x of the vector's coordinates
+// and K the per-vector scale with the sign the caller's transform leaves on y folded in
+// (bits <= 2: NX = fma(y, -K, +0) is the value in stage-1 units with its sign flipped;
+// bits >= 3: w1 = fma(y, K, +0)). K2 = |K| r12 (bits <= 2) and K2s (bits >= 3, carrying the
+// same sign as K) are the stage-2 scales; t1s / t2s are the LDS bucket tables (bits >= 3).
+template <int BITS, int STAGES, int JLO, int JHI, int N>
+__device__ __forceinline__ void quantize_run(const float (&y)[N], float K, float K2, float K2s, const EncodeArgs& a,
+                                             const float4* t1s, const float2* t2s, uint32_t& w1o, uint32_t& w2o) {
+  constexpr int jlo = JLO, jhi = JHI, cnt = jhi - jlo;
+  static_assert(0 <= JLO && JLO < JHI && JHI <= N, "code range inside the values");
+  uint32_t u1 = 0, u2 = 0;
+#pragma unroll
+  for (int j = jhi - 1; j >= jlo; --j) {  // highest code first: code jlo ends in bits [0, BITS)
+    // STAGES = 0 takes +K: then the sign bit is [y_true < 0] (zeros of either sign give
+    // +0), and the word is complemented below to [y_true >= 0]
+    const float nx = __builtin_fmaf(y[j], STAGES == 0 ? K : -K, 0.0f);
+    const float ax = __builtin_fabsf(nx);
+    if constexpr (BITS == 1) {
+      // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
+      u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
+      const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -a.cm2[0]);
+      u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
+    } else if constexpr (BITS == 2) {
+      // Unit 2/T1: bit 31 of NX is P = [y > 0], bit 30 is O = [|NX| >= 2] = [|y| >= T1].
+      u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 30);
+      // U = |NX| - 2 is |y| - T1 in units 2/T1. T1 is the midpoint of the two centroid
+      // magnitudes c0 < c1, so the residual magnitude |y| - c (c the nearer one) is
+      // sign(U) * (|U| T1/2 - h), h = (c1 - c0)/2. W = (|U| T1/2 - h) in stage-2 units
+      // 2/T2 = |U| r12 - cm2[0]: its bit 31 is sign(W), bit 30 is [|W| >= 2] = [|r| >= T2].
+      const float u = ax - 2.0f;
+      const float w = __builtin_fmaf(__builtin_fabsf(u), a.r12, -a.cm2[0]);
+      u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(w), 30);
+    } else {
+      // Bucket tables: the code is base + [w > thr] of the entry that the bucket of
+      // v = clamp(w + 1/2, 0, 1) selects (the clamp is the add's output modifier). The
+      // entry's byte offset is read from the bits of v + 2^13 (spacing 2^-10: sixteen
+      // times the bucket count) and of v2 + 2^14 (spacing 2^-9, eight-byte entries).
+      const float w1 = __builtin_fmaf(y[j], K, 0.0f);
+      const float v1 = __builtin_amdgcn_fmed3f(w1 + 0.5f, 0.0f, 1.0f);
+      const uint32_t o1 = __float_as_uint(v1 + 8192.0f) & 0x7F0u;
+      const float4 e = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(t1s) + o1);
+      const bool gt = w1 > e.x;
+      u1 = (u1 << BITS) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
+      const float w2 = __builtin_fmaf(y[j], K2s, gt ? e.w : e.z);
+      const float v2 = __builtin_amdgcn_fmed3f(w2 + 0.5f, 0.0f, 1.0f);
+      const uint32_t o2 = __float_as_uint(v2 + 16384.0f) & 0x3F8u;
+      const float2 e2 = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(t2s) + o2);
+      u2 = (u2 << BITS) | (__float_as_uint(e2.y) + (w2 > e2.x ? 1u : 0u));
+    }
+  }
+  // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
+  // Q = [residual magnitude < 0] for stage 2. Stage 2's sign is P2 = P1 xor Q (the
+  // residual of a non-positive y is the negated magnitude). A field with P = 0 counts
+  // downward from the middle: its low bits are (2^(BITS-1) - 1) - m = m xor
+  // (2^(BITS-1) - 1); at BITS = 2 that low bit is O xor P xor 1 from the [>= T] bit the
+  // alignbit stored.
+  // (BITS >= 3 fields are the codes themselves.)
+  const uint32_t ones = field_ones<BITS>(cnt);
+  if constexpr (BITS == 2) {
+    // stage 2 holds (sign(W), [|W| >= 2]); its residual-magnitude sign is
+    // Q = sign(U) xor sign(W) with sign(U) = not O, so P2 = P xor not O xor sign(W)
+    u2 ^= ((u1 ^ (u1 >> 1) ^ ones) & ones) << 1;
+    u1 ^= ~(u1 >> 1) & ones;
+    u2 ^= ~(u2 >> 1) & ones;
+  } else if constexpr (BITS == 1) {
+    u2 ^= u1;
+  }
+  if constexpr (STAGES == 0) u1 = ~u1 & ones;
+  w1o = u1;
+  w2o = u2;
+}
+
 // ------------------------------------------------------------------------------ encode
 
 // STAGES = 2: the two-stage residual codec (both code streams); STAGES = 1: the single-stage
@@ -272,67 +347,7 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     // Codes of this lane's coordinates [jlo, jhi) of both stages, LSB-first with code jlo in
     // bits [0, BITS) (as one packed word holds them).
     auto pack_range = [&](auto first, auto end, uint32_t& w1o, uint32_t& w2o) {
-      constexpr int jlo = decltype(first)::value, jhi = decltype(end)::value, cnt = jhi - jlo;
-      uint32_t u1 = 0, u2 = 0;
-#pragma unroll
-      for (int j = jhi - 1; j >= jlo; --j) {  // highest code first: code jlo ends in bits [0, BITS)
-        // STAGES = 0 takes +K: then the sign bit is [y_true < 0] (zeros of either sign give
-        // +0), and the word is complemented below to [y_true >= 0]
-        const float nx = __builtin_fmaf(y[j], STAGES == 0 ? K : -K, 0.0f);
-        const float ax = __builtin_fabsf(nx);
-        if constexpr (BITS == 1) {
-          // stage 1: [y > 0] is the sign bit of NX; stage 2: sign of the residual magnitude
-          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 31);
-          const float x2 = __builtin_fmaf(__builtin_fabsf(y[j]), K2, -a.cm2[0]);
-          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(x2), 31);
-        } else if constexpr (BITS == 2) {
-          // Unit 2/T1: bit 31 of NX is P = [y > 0], bit 30 is O = [|NX| >= 2] = [|y| >= T1].
-          u1 = __builtin_amdgcn_alignbit(u1, __float_as_uint(nx), 30);
-          // U = |NX| - 2 is |y| - T1 in units 2/T1. T1 is the midpoint of the two centroid
-          // magnitudes c0 < c1, so the residual magnitude |y| - c (c the nearer one) is
-          // sign(U) * (|U| T1/2 - h), h = (c1 - c0)/2. W = (|U| T1/2 - h) in stage-2 units
-          // 2/T2 = |U| r12 - cm2[0]: its bit 31 is sign(W), bit 30 is [|W| >= 2] = [|r| >= T2].
-          const float u = ax - 2.0f;
-          const float w = __builtin_fmaf(__builtin_fabsf(u), a.r12, -a.cm2[0]);
-          u2 = __builtin_amdgcn_alignbit(u2, __float_as_uint(w), 30);
-        } else {
-          // Bucket tables: the code is base + [w > thr] of the entry that the bucket of
-          // v = clamp(w + 1/2, 0, 1) selects (the clamp is the add's output modifier). The
-          // entry's byte offset is read from the bits of v + 2^13 (spacing 2^-10: sixteen
-          // times the bucket count) and of v2 + 2^14 (spacing 2^-9, eight-byte entries).
-          const float w1 = __builtin_fmaf(y[j], K, 0.0f);
-          const float v1 = __builtin_amdgcn_fmed3f(w1 + 0.5f, 0.0f, 1.0f);
-          const uint32_t o1 = __float_as_uint(v1 + 8192.0f) & 0x7F0u;
-          const float4 e = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(t1s) + o1);
-          const bool gt = w1 > e.x;
-          u1 = (u1 << BITS) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
-          const float w2 = __builtin_fmaf(y[j], K2s, gt ? e.w : e.z);
-          const float v2 = __builtin_amdgcn_fmed3f(w2 + 0.5f, 0.0f, 1.0f);
-          const uint32_t o2 = __float_as_uint(v2 + 16384.0f) & 0x3F8u;
-          const float2 e2 = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(t2s) + o2);
-          u2 = (u2 << BITS) | (__float_as_uint(e2.y) + (w2 > e2.x ? 1u : 0u));
-        }
-      }
-      // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
-      // Q = [residual magnitude < 0] for stage 2. Stage 2's sign is P2 = P1 xor Q (the
-      // residual of a non-positive y is the negated magnitude). A field with P = 0 counts
-      // downward from the middle: its low bits are (2^(BITS-1) - 1) - m = m xor
-      // (2^(BITS-1) - 1); at BITS = 2 that low bit is O xor P xor 1 from the [>= T] bit the
-      // alignbit stored.
-      // (BITS >= 3 fields are the codes themselves.)
-      const uint32_t ones = field_ones<BITS>(cnt);
-      if constexpr (BITS == 2) {
-        // stage 2 holds (sign(W), [|W| >= 2]); its residual-magnitude sign is
-        // Q = sign(U) xor sign(W) with sign(U) = not O, so P2 = P xor not O xor sign(W)
-        u2 ^= ((u1 ^ (u1 >> 1) ^ ones) & ones) << 1;
-        u1 ^= ~(u1 >> 1) & ones;
-        u2 ^= ~(u2 >> 1) & ones;
-      } else if constexpr (BITS == 1) {
-        u2 ^= u1;
-      }
-      if constexpr (STAGES == 0) u1 = ~u1 & ones;
-      w1o = u1;
-      w2o = u2;
+      quantize_run<BITS, STAGES, decltype(first)::value, decltype(end)::value>(y, K, K2, K2s, a, t1s, t2s, w1o, w2o);
     };
     if constexpr (!STAGED) {
       static_for<0, NWL>([&](auto wi) {
@@ -389,6 +404,263 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     }
     v0_prev = v0;
     nv_prev = nv;
+  }
+  store_prev();
+}
+
+// ------------------------------------------------------------------------------ encode, matrix cores
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte r of kWalsh8 holds bit t = parity(r & t) for r, t < 8: the eight Walsh functions of
+// length 8, i.e. the sign pattern of row r of the 8 x 8 Sylvester Hadamard matrix.
+constexpr uint64_t kWalsh8 = 0x963C5AF066CCAA00ull;
+
+// The encode of D = 128 with its transform on the matrix cores. The Sylvester matrix
+// factors as H_128 = H_4 (x) H_32: entry (32 g + r, 32 k + c) is (-1)^popcount(g & k) H_32[r][c].
+// So each 32-coordinate input block x_k of a vector is first transformed on its own,
+// z_k = H_32 x_k, and output block g is sum_k (-1)^popcount(g & k) z_k: two more butterfly
+// stages across the blocks. For a tile of 16 vectors the z_k are 8 products
+// v_mfma_f32_16x16x32_f16 (A = a 16 x 32 slice of H_32, B = input block k of the 16 vectors),
+// whose +-1 entries and fp16 inputs multiply exactly, summed in float32; the stages across
+// the blocks are float32 adds in registers. The rotation's signs diag(s) are applied to the
+// fp16 inputs first (an XOR of sign bits), as the butterfly kernel does through its weights.
+//
+// Why the matrix cores: the butterfly kernel spends about 6.5 VALU instructions per
+// coordinate on the transform, as many as its quantizers and packing together, and a wave's
+// last tile is computed after the input stream has ended; here the transform is 8 MFMAs and
+// 64 adds per 16-vector tile, about 280 VALU instructions in all against 450, which shortens
+// both the arithmetic that the memory stream has to hide and that tail.
+//
+// MFMA layout (16x16x32): lane l supplies row l % 16 of A and column l % 16 of B, each with
+// the 8 k-values 8 (l / 16) + [0, 8), and receives D[4 (l / 16) + i][l % 16], i < 4. B's
+// columns are the tile's vectors: lane l works on vector v = l % 16 together with the lanes
+// of the same v in the other three groups g = l / 16, and supplies the coordinates
+// 32 k + 8 g + [0, 8) of input block k (one 16-byte chunk). A's row m of output half mh
+// carries H_32 row 8 (m >> 2) + 4 mh + (m & 3), so that lane group g receives the block
+// coordinates 8 g + 4 mh + i: over the two halves, 8 consecutive coordinates of every block,
+// and of every output block after the stages across blocks. Their codes are 8 consecutive
+// fields of one packed word (BITS = 4) or a quarter or half of one (BITS = 1, 2); a 4 x 4
+// transpose of those pieces across the four lane groups (v_permlane32_swap, then
+// v_permlane16_swap) leaves lane group g with the vector's words [g NW / 4, (g + 1) NW / 4),
+// stored as one contiguous run.
+template <int BITS, bool CONTIG, int STAGES>
+__global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_kernel(const EncodeArgs a) {
+  constexpr int D = 128;
+  constexpr int NB = D / 32;             // 32-coordinate blocks of a vector
+  constexpr int CPV = D / 8;             // 16-byte chunks per vector
+  constexpr int TV = kMxTile;            // vectors per tile: the MFMA's 16 columns
+  constexpr int TCH = TV * CPV;          // chunks per tile
+  constexpr int EPW = 32 / BITS;         // codes per word
+  constexpr int NW = D / EPW;            // words per vector per stream
+  constexpr int WPL = NW / 4;            // words each lane group stores per stream
+  constexpr bool TWO = STAGES == 2;
+  static_assert(TV == 16 && NB == 4, "16 vectors of 4 blocks: one MFMA column per vector, one lane group per block");
+  static_assert(BITS == 1 || BITS == 2 || BITS == 4, "codes that tile a word");
+  static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
+
+  __shared__ u32x4_t stage[kWavesPerBlock][TCH];
+  constexpr int TSLOTS = BITS >= 3 ? 128 : 1;
+  __shared__ float4 t1s[TSLOTS];
+  __shared__ float2 t2s[TSLOTS];
+  if constexpr (BITS >= 3) {
+    for (int i = threadIdx.x; i < TSLOTS; i += kBlockThreads) {
+      const bool in = i < kTabEntries;
+      t1s[i] = in ? make_float4(a.tab1[i][0], a.tab1[i][1], a.tab1[i][2], a.tab1[i][3])
+                  : make_float4(__builtin_inff(), 0.f, 0.f, 0.f);
+      t2s[i] = in ? make_float2(a.tab2[i][0], a.tab2[i][1]) : make_float2(__builtin_inff(), 0.f);
+    }
+    __syncthreads();
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int v = lane & 15;  // this lane's vector in the tile
+  const int g = lane >> 4;  // its lane group: input coordinates 32 k + 8 g + [0, 8)
+  u32x4_t* buf = stage[wv];
+  const int n_tiles = static_cast<int>((a.n_vec + TV - 1) / TV);  // fits (checked on the host)
+  const int stride = static_cast<int>(gridDim.x) * kWavesPerBlock;
+  const char* xb = reinterpret_cast<const char*>(a.x);
+
+  // Direct-to-LDS loads of tile t: instruction k fills slots [64k, 64k + 64); slot s holds
+  // chunk (s % CPV) ^ row of vector row = s / CPV, so the 8 lanes of an LDS read phase
+  // (consecutive vectors, one chunk each) hit 8 distinct 16-byte bank groups. Rows past the
+  // input's end re-read its last vector: every load stays inside the input, and those rows
+  // are never stored.
+  auto dma = [&](int t) {
+    const int64_t t0 = static_cast<int64_t>(t) * TV;
+    const int nv = static_cast<int>(a.n_vec - t0 < TV ? a.n_vec - t0 : TV);
+    const char* base = xb + t0 * (2 * D);  // wave-uniform
+#pragma unroll
+    for (int k = 0; k < TCH / 64; ++k) {
+      const int s = k * 64 + lane, r = s / CPV, p = s % CPV;
+      const int rr = (nv == TV || r < nv) ? r : nv - 1;
+      const uint32_t off = static_cast<uint32_t>(rr * CPV + (p ^ r)) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, kNonTemporal);
+    }
+  };
+
+  int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
+  if (tile < n_tiles) dma(tile);
+
+  // Per-wave constants, computed while the first tile is in flight: the sign-bit masks of
+  // diag(s) over this lane's input chunks 4 k + g, and the A operands of the two output
+  // halves (row m = v: H_32 row 8 (v >> 2) + 4 mh + (v & 3) at columns 8 g + t, t < 8, as
+  // fp16 +-1 pairs).
+  u32x4_t mk[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mk[k][i] = a.wpair[4 * (4 * k + g) + i] ^ kOnePair;
+  f16x8_t ah[2];
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) {
+    const int r = 8 * (v >> 2) + 4 * mh + (v & 3);
+    const uint32_t pat = static_cast<uint32_t>(kWalsh8 >> (8 * (r & 7))) & 0xFFu;
+    const uint32_t f = (__builtin_popcount((r >> 3) & g) & 1) ? 0x80008000u : 0u;
+    u32x4_t w;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      w[p] = (kOnePair | (((pat >> (2 * p)) & 1u) << 15) | (((pat >> (2 * p + 1)) & 1u) << 31)) ^ f;
+    ah[mh] = __builtin_bit_cast(f16x8_t, w);
+  }
+
+  // The previous tile's words wait in registers until this tile has left LDS, so the
+  // loop-top wait (which counts stores too) covers stores issued a compute phase earlier.
+  uint32_t o1[WPL], o2[WPL];
+  float n_prev = 0.f;
+  int64_t row_prev = -1;  // -1: nothing to store (first tile, or a lane past the last vector)
+  auto store_prev = [&]() {
+    if (row_prev >= 0) {
+      if (g == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
+      store_words<WPL>(a.p1 + row_prev * NW + g * WPL, o1);
+      if constexpr (TWO) store_words<WPL>(a.p2 + row_prev * NW + g * WPL, o2);
+    }
+  };
+
+  for (; tile < n_tiles; tile += stride) {
+    const int64_t v0 = static_cast<int64_t>(tile) * TV;
+    const int nv = static_cast<int>(a.n_vec - v0 < TV ? a.n_vec - v0 : TV);
+
+    // 1. This lane's fp16 coordinates: chunk 4 k + g of its vector is its B operand of input
+    //    block k.
+    wait_vmem();
+    u32x4_t bq[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) bq[k] = buf[v * CPV + ((4 * k + g) ^ v)];
+    wait_lds();
+
+    // 2. Store the previous tile, then load the next one into the buffer just read.
+    store_prev();
+    if (tile + stride < n_tiles) dma(tile + stride);
+
+    // 3. diag(s) on the fp16 inputs, the blocks' transforms z_k (register i of half mh is
+    //    block coordinate 8 g + 4 mh + i), then the two stages across the blocks: output block
+    //    gb = sum_k (-1)^popcount(gb & k) z_k.
+    f32x4_t y4[NB][2];
+    {
+      f32x4_t z[NB][2];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const f16x8_t bx = __builtin_bit_cast(f16x8_t, bq[k] ^ mk[k]);
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh) z[k][mh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mh], bx, f32x4_t{}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s0 = z[0][mh][i] + z[1][mh][i], d0 = z[0][mh][i] - z[1][mh][i];
+          const float s1 = z[2][mh][i] + z[3][mh][i], d1 = z[2][mh][i] - z[3][mh][i];
+          y4[0][mh][i] = s0 + s1;
+          y4[1][mh][i] = d0 + d1;
+          y4[2][mh][i] = s0 - s1;
+          y4[3][mh][i] = d0 - d1;
+        }
+    }
+
+    // 4. Norm: squares of the fp16 values summed in float32, the four lane groups of the
+    //    vector added in a fixed order (every lane forms the same sum).
+    float ss;
+    {
+      float s2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t e = bq[k][i];
+          const half2_t p = __builtin_bit_cast(half2_t, e);
+          s2[i & 1] = __builtin_amdgcn_fdot2(p, p, s2[i & 1], false);
+        }
+      }
+      const float part = s2[0] + s2[1];
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      const float p2 = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);  // groups g and g ^ 2
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p2), false, false);
+      ss = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);              // and g ^ 1
+    }
+    const float n = __builtin_amdgcn_sqrtf(ss);  // v_sqrt_f32, within 1 ulp
+    float K, K2 = 0.f, K2s = 0.f;
+    if constexpr (BITS >= 3) {
+      const double rs = (ss > 0.f) ? __builtin_amdgcn_rsq(static_cast<double>(ss)) : 0.0;
+      K = static_cast<float>(static_cast<double>(a.k_scale) * rs);
+      K2s = static_cast<float>(static_cast<double>(a.k2_scale) * rs);
+    } else {
+      K = (n > 0.f) ? a.k_scale * __builtin_amdgcn_rcpf(n) : 0.f;
+      K2 = K * a.r12;
+    }
+
+    // 5. Codes: output block gb's coordinates 8 g + [0, 8) of this lane give piece gb
+    //    (8 BITS bits).
+    uint32_t pc1[NB], pc2[NB];
+#pragma unroll
+    for (int gb = 0; gb < NB; ++gb) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = y4[gb][0][i];
+        y[4 + i] = y4[gb][1][i];
+      }
+      quantize_run<BITS, STAGES, 0, 8>(y, K, K2, K2s, a, t1s, t2s, pc1[gb], pc2[gb]);
+    }
+
+    // 6. Transpose the pieces across the lane groups: piece gb of group g' goes to group gb,
+    //    slot g' (two swaps across lane halves, then two across 16-lane rows), so group g
+    //    holds the pieces of output block g from groups 0..3 in order, i.e. the vector's
+    //    words [g WPL, g WPL + WPL) once joined.
+    auto gather = [&](const uint32_t (&pc)[NB], uint32_t (&o)[WPL]) {
+      uint32_t w[4] = {pc[0], pc[1], pc[2], pc[3]};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(w[j], w[j + 2], false, false);
+        w[j] = sw[0];
+        w[j + 2] = sw[1];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(w[j], w[j + 1], false, false);
+        w[j] = sw[0];
+        w[j + 1] = sw[1];
+      }
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = w[j];
+      } else if constexpr (BITS == 2) {
+        o[0] = w[0] | (w[1] << 16);
+        o[1] = w[2] | (w[3] << 16);
+      } else {
+        o[0] = w[0] | (w[1] << 8) | (w[2] << 16) | (w[3] << 24);
+      }
+    };
+    gather(pc1, o1);
+    if constexpr (TWO) gather(pc2, o2);
+
+    n_prev = n;
+    {
+      const int64_t r = cache_row<CONTIG>(a.map, v0, v);
+      row_prev = (v < nv) ? r : -1;
+    }
   }
   store_prev();
 }
@@ -527,47 +799,76 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
 
 // ------------------------------------------------------------------------------ dispatch
 
-// Blocks of one kernel resident on the whole current device at once.
-static int resident_blocks(const void* f) {
+// Compute units of the current device and blocks of one kernel resident per CU.
+static bool residency(const void* f, int* cus, int* per_cu) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kBlockThreads, 0) != hipSuccess) return 0;
-  return cus * (per_cu > 0 ? per_cu : 1);
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, f, kBlockThreads, 0) != hipSuccess) return false;
+  if (*per_cu < 1) *per_cu = 1;
+  return *cus > 0;
 }
 
-// Persistent grid: as many blocks as fit on the device at once (every wave resident from
-// the start, walking tiles with a grid stride and loading its next tile while it computes
-// the current one), fewer if there are fewer tiles. The resident count is cached per
-// kernel (one value per process; all MI355X devices have the same count).
-static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* cap, hipStream_t stream) {
+// Persistent grid: at most as many blocks as fit on the device at once (every wave resident
+// from the start, walking tiles with a grid stride and loading its next tile while it
+// computes the current one), fewer if there are fewer tiles. The residency is asked once per
+// kernel (one value per process; all MI355X devices have the same counts).
+//
+// A wave's last tile is computed after the input stream has ended, so a launch ends with the
+// last round's arithmetic on the busiest SIMD. With balance set, the grid takes the number
+// of resident blocks per CU (from the most that fit down to 2) whose last round puts the
+// fewest waves on one SIMD (a block's waves sit on the four SIMDs of its CU), preferring
+// more blocks on ties: 16384 tiles on 256 CUs run as 3 blocks per CU (5 rounds of 3072
+// waves and a last round of 1024, one wave per SIMD) rather than 4 (4 full rounds).
+static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* cap, bool balance,
+                         hipStream_t stream) {
   const int64_t tiles = (n_vec + vw - 1) / vw;
   if (tiles > INT_MAX) return hipErrorInvalidValue;
-  if (*cap <= 0) *cap = resident_blocks(f);  // a benign race: every caller computes the same value
-  if (*cap <= 0) return hipErrorInvalidValue;
+  // cap[0]: CUs, cap[1]: resident blocks per CU (a benign race: every caller computes the same)
+  if (cap[0] <= 0 && !residency(f, &cap[0], &cap[1])) return hipErrorInvalidValue;
+  const int64_t cus = cap[0], per_cu = cap[1];
   const int64_t want = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int blocks = static_cast<int>(want < *cap ? want : *cap);
+  int64_t blocks = cus * per_cu;
+  if (balance && want > blocks) {
+    int64_t best_last = INT64_MAX;
+    const int64_t kmin = per_cu < 2 ? per_cu : 2;
+    for (int64_t k = per_cu; k >= kmin; --k) {
+      const int64_t waves = cus * k * kWavesPerBlock;
+      const int64_t last = tiles - ((tiles + waves - 1) / waves - 1) * waves;  // tiles of the last round
+      const int64_t per_simd = (last + cus * kWavesPerBlock - 1) / (cus * kWavesPerBlock);
+      if (per_simd < best_last) {
+        best_last = per_simd;
+        blocks = cus * k;
+      }
+    }
+  }
+  if (want < blocks) blocks = want;
   void* a[] = {args};
-  return hipLaunchKernel(f, dim3(blocks), dim3(kBlockThreads), a, 0, stream);
+  return hipLaunchKernel(f, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), a, 0, stream);
 }
 
 template <int D, int BITS, int STAGES>
 static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
-  static int cap[2] = {0, 0};
+  static int cap[2][2] = {{0, 0}, {0, 0}};
   const bool c = a.map.contiguous != 0;
-  const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES>)
-                    : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES>);
-  return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, &cap[c ? 1 : 0], stream);
+  if constexpr (encode_on_matrix_cores(D, BITS)) {
+    const void* f = c ? reinterpret_cast<const void*>(&encode_mx_kernel<BITS, true, STAGES>)
+                      : reinterpret_cast<const void*>(&encode_mx_kernel<BITS, false, STAGES>);
+    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, kMxTile, cap[c ? 1 : 0], true, stream);
+  } else {
+    const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES>)
+                      : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES>);
+    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
+  }
 }
 
 template <int D, int BITS, int STAGES>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  static int cap[2] = {0, 0};
+  static int cap[2][2] = {{0, 0}, {0, 0}};
   const bool c = a.map.contiguous != 0;
   const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES>)
                     : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES>);
-  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, &cap[c ? 1 : 0], stream);
+  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
 }
 
 #define KVQ_FOR_BITS(MACRO, D, S) \

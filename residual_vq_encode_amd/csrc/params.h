@@ -26,6 +26,22 @@ constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 1.0 values
 constexpr int kTabBuckets = 64;
 constexpr int kTabEntries = kTabBuckets + 1;
 
+// Vectors per wave tile of the matrix-core encode (the 16 columns of its MFMA).
+constexpr int kMxTile = 16;
+
+// The encode of D = 128 at 1, 2 and 4 bits runs its transform on the matrix cores; every
+// other shape takes the butterfly kernel.
+constexpr bool encode_on_matrix_cores(int d, int bits) { return d == 128 && bits != 3; }
+
+// Vectors per wave tile (the unit of work of the persistent grids, indexed with 32-bit
+// integers): the matrix-core encode takes 32; the butterfly kernels spread a vector over
+// d / min(d, 32) lanes of a 64-lane wave.
+constexpr int64_t butterfly_tile_vectors(int d) { return 64 / (d / (d < 32 ? d : 32)); }
+constexpr int64_t encode_tile_vectors(int d, int bits) {
+  return encode_on_matrix_cores(d, bits) ? kMxTile : butterfly_tile_vectors(d);
+}
+constexpr int64_t decode_tile_vectors(int d) { return butterfly_tile_vectors(d); }
+
 // Where token s of (b, h) lands in a cache whose token axis has capacity S_cap:
 // row(v) = (v / S) * S_cap + s_offset + v % S for the flattened input index v.
 struct RowMap {
