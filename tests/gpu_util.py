@@ -26,6 +26,20 @@ def flip_cap(n_codes: int) -> float:
     of fewer than 10^6 codes would be held to zero flips by the literal fraction, so such
     samples may carry one in-window, one-level flip; larger ones get the rate itself."""
     return max(MAX_FLIP_FRACTION, 1.0 / max(1, n_codes))
+
+
+# Every sample judged under flip_cap in this session, pooled: one allowed flip per small
+# sample must not add up to a rate above the cap over all of them together
+# (tests/test_zy_pooled_flips.py checks the pool after the other GPU tests).
+POOLED = {"flips": 0, "codes": 0, "samples": 0}
+
+
+def capped(n_codes: int, flips: int) -> float:
+    """flip_cap(n_codes) for a sample with `flips` differing codes, recorded in POOLED."""
+    POOLED["flips"] += int(flips)
+    POOLED["codes"] += int(n_codes)
+    POOLED["samples"] += 1
+    return flip_cap(n_codes)
 NORM_REL_TOL = 1e-6
 # Decode: on unit vectors (norms = NULL) the device and oracle reconstructions differ by
 # float32 butterfly rounding plus at most one float16 ulp (2^-11 for |x| < 1).
@@ -75,6 +89,31 @@ def judge(x16_rows: np.ndarray, signs, bits, p1_rows: np.ndarray, p2_rows: np.nd
     return flips.compare_encode(p1_rows, p2_rows, norm_rows, ref, t, REL_WINDOW), ref
 
 
+def judge_all(x_rows: torch.Tensor, signs, bits, p1_rows: torch.Tensor, p2_rows: torch.Tensor,
+              norm_rows: torch.Tensor, chunk: int = 1 << 18):
+    """Every row of a large launch judged against the oracle, chunk by chunk (the oracle's
+    memory stays bounded); the chunks' counts add up to one report over all rows."""
+    d = x_rows.shape[1]
+    t = tables(d, bits)
+    s8 = np.asarray(signs, np.int8)
+    total = flips.Report(n_vectors=0, n_codes=0)
+    for r0 in range(0, x_rows.shape[0], chunk):
+        r1 = min(x_rows.shape[0], r0 + chunk)
+        ref = rvq.encode(x_rows[r0:r1].cpu().numpy(), s8, t)
+        rep = flips.compare_encode(as_u32(p1_rows[r0:r1]), as_u32(p2_rows[r0:r1]), norm_rows[r0:r1].cpu().numpy(),
+                                   ref, t, REL_WINDOW)
+        total.n_vectors += rep.n_vectors
+        total.n_codes += rep.n_codes
+        total.stage1_diff += rep.stage1_diff
+        total.stage2_diff += rep.stage2_diff
+        total.bad_stage1 += rep.bad_stage1
+        total.bad_stage2 += rep.bad_stage2
+        total.padding_bad += rep.padding_bad
+        total.norm_max_rel = max(total.norm_max_rel, rep.norm_max_rel)
+        total.examples += [(r0 + e[1],) + tuple(e) for e in rep.examples[:2]]
+    return total
+
+
 def check_encode(x: torch.Tensor, signs, bits, max_flip=None):
     """Encode x on the GPU and require the oracle's codes and norms under the rule.
     max_flip=None applies flip_cap(); degenerate inputs pass 0.0 (no flips at all)."""
@@ -83,7 +122,7 @@ def check_encode(x: torch.Tensor, signs, bits, max_flip=None):
     x_rows = x.detach().cpu().numpy().reshape(-1, D)
     rep, ref = judge(x_rows, signs, bits, as_u32(p1).reshape(-1, p1.shape[-1]),
                      as_u32(p2).reshape(-1, p2.shape[-1]), nrm.cpu().numpy().reshape(-1))
-    cap = flip_cap(rep.n_codes) if max_flip is None else max_flip
+    cap = capped(rep.n_codes, rep.flips) if max_flip is None else max_flip
     assert rep.ok(cap, NORM_REL_TOL), rep.summary()
     return rep, (p1, p2, nrm), ref
 
@@ -135,7 +174,7 @@ def check_encode_mse(x: torch.Tensor, signs, bits, max_flip=None, S_cap=None, s_
     win_p = as_u32(p[:, :, s_offset:s_offset + S]).reshape(-1, cb.n_words)
     win_n = nrm[:, :, s_offset:s_offset + S].cpu().numpy().reshape(-1)
     rep = flips.compare_encode_single(win_p, win_n, ref, t, REL_WINDOW)
-    cap = flip_cap(rep.n_codes) if max_flip is None else max_flip
+    cap = capped(rep.n_codes, rep.flips) if max_flip is None else max_flip
     assert rep.ok(cap, NORM_REL_TOL), rep.summary()
     return rep, (p, nrm), ref
 

@@ -57,7 +57,7 @@ def check_rabitq(x, signs, S_cap=None, s_offset=0, max_flip=None):
     assert not (pw & packing.padding_mask(D, 1)[None, :]).any(), "padding bits must be zero"
     diff = packing.unpack(pw, 1, D) != ref["bits"]
     n_diff = int(diff.sum())
-    cap = gu.flip_cap(diff.size) if max_flip is None else max_flip
+    cap = gu.capped(diff.size, int(diff.sum())) if max_flip is None else max_flip
     assert n_diff <= cap * diff.size, (n_diff, diff.size)
     if n_diff:
         assert np.all(np.abs(ref["y"][diff]) <= 1e-5 / math.sqrt(D)), "bit differs outside the window"
