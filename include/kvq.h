@@ -252,6 +252,28 @@ kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, co
 kvq_status kvq_rvq_attend_workspace_size(int32_t d, int32_t bits, int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
                                          int64_t S_kv, int64_t* bytes);
 
+/*
+ * kvq_rvq_attend_noalloc - device. kvq_rvq_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same checks, kernels and result, with the partial results in a device
+ * scratch array the library holds instead of a caller's workspace. Arguments as for
+ * kvq_rvq_attend, without workspace and workspace_bytes.
+ *   Scratch: KVQ_ATTEND_SCRATCH_BYTES (32 MiB) per device, part of the library's code object
+ *   (each device the library runs on holds one copy until the process ends). Its address is
+ *   looked up at the first call on each device. Nothing in it needs clearing between calls.
+ *   Every call on one device uses that device's copy: calls that overlap on one device (on
+ *   different streams, or from several threads) race and must be ordered by the caller.
+ * Errors: as kvq_rvq_attend, and KVQ_ERR_RANGE when these sizes need more than
+ * KVQ_ATTEND_SCRATCH_BYTES (kvq_rvq_attend_workspace_size tells how much), checked on the
+ * host before any HIP call. Nothing is allocated or freed.
+ */
+#define KVQ_ATTEND_SCRATCH_BYTES (32ll << 20)
+kvq_status kvq_rvq_attend_noalloc(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
+                                  int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
+                                  const uint32_t* k_packed1, const uint32_t* k_packed2, const float* k_norms,
+                                  const uint32_t* v_packed1, const uint32_t* v_packed2, const float* v_norms,
+                                  int64_t S_cap, int64_t S_kv, float scale, uint16_t* out, void* stream);
+
 /* Static text for a status code; never NULL. */
 const char* kvq_status_str(kvq_status status);
 

@@ -27,7 +27,7 @@ from typing import Optional
 __all__ = [
     "KvqError", "Codebooks", "load", "library_path", "build_codebooks", "kvq_build_codebooks",
     "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_mse_encode_pack", "kvq_mse_unpack_decode",
-    "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_rabitq_encode_pack", "kvq_qjl_encode_pack",
+    "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_rvq_attend_noalloc", "ATTEND_SCRATCH_BYTES", "kvq_rabitq_encode_pack", "kvq_qjl_encode_pack",
     "kvq_qjl_supported", "kvq_status_str", "encode", "decode", "encode_mse", "decode_mse", "encode_rabitq",
     "encode_qjl", "attend", "n_words",
 ]
@@ -101,6 +101,9 @@ def load() -> ctypes.CDLL:
     lib.kvq_rvq_attend.argtypes = [ctypes.POINTER(Codebooks), ctypes.POINTER(Codebooks), ptr, i64, i64, i64, i64,
                                    ptr, ptr, ptr, ptr, ptr, ptr, i64, i64, ctypes.c_float, ptr, i64, ptr, ptr]
     lib.kvq_rvq_attend.restype = ctypes.c_int
+    lib.kvq_rvq_attend_noalloc.argtypes = [ctypes.POINTER(Codebooks), ctypes.POINTER(Codebooks), ptr, i64, i64, i64,
+                                           i64, ptr, ptr, ptr, ptr, ptr, ptr, i64, i64, ctypes.c_float, ptr, ptr]
+    lib.kvq_rvq_attend_noalloc.restype = ctypes.c_int
     lib.kvq_rvq_attend_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, i64, i64, i64, i64, i64,
                                                    ctypes.POINTER(ctypes.c_int64)]
     lib.kvq_rvq_attend_workspace_size.restype = ctypes.c_int
@@ -322,6 +325,35 @@ def kvq_rvq_attend(cbk: Codebooks, cbv: Codebooks, q, kcache, vcache, S_kv: int,
     _check(load().kvq_rvq_attend(ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q), B, Hq, Sq, Hkv, _ptr(k1), _ptr(k2),
                                  _ptr(kn), _ptr(v1), _ptr(v2), _ptr(vn), S_cap, int(S_kv), float(scale),
                                  _ptr(workspace), nbytes, _ptr(out), _stream_handle(stream)), "kvq_rvq_attend")
+
+
+# Device scratch behind kvq_rvq_attend_noalloc (KVQ_ATTEND_SCRATCH_BYTES in include/kvq.h).
+ATTEND_SCRATCH_BYTES = 32 << 20
+
+
+def kvq_rvq_attend_noalloc(cbk: Codebooks, cbv: Codebooks, q, kcache, vcache, S_kv: int, scale: float, out,
+                           stream=None) -> None:
+    """kvq_rvq_attend without a workspace: the partial results go to the library's per-device
+    scratch (at most ATTEND_SCRATCH_BYTES; larger plans raise KVQ_ERR_RANGE). Nothing is
+    allocated; calls that overlap on one device share the scratch and race."""
+    import torch
+    k1, k2, kn = kcache
+    v1, v2, vn = vcache
+    _require_cuda(q, k1, k2, kn, v1, v2, vn, out)
+    if q.dtype != torch.float16 or q.dim() != 4 or not q.is_contiguous() or q.shape[3] != cbk.d:
+        raise ValueError("q must be a contiguous fp16 [B, Hq, Sq, d] tensor")
+    if out.dtype != torch.float16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q")
+    B, Hq, Sq, _ = q.shape
+    Hkv, S_cap = k1.shape[1], k1.shape[2]
+    for name, t in (("k_packed1", k1), ("k_packed2", k2), ("v_packed1", v1), ("v_packed2", v2)):
+        _check_stream(cbk, name, t, B, Hkv, S_cap)
+    for name, t in (("k_norms", kn), ("v_norms", vn)):
+        if tuple(t.shape) != (B, Hkv, S_cap) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 {(B, Hkv, S_cap)}")
+    _check(load().kvq_rvq_attend_noalloc(ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q), B, Hq, Sq, Hkv, _ptr(k1),
+                                         _ptr(k2), _ptr(kn), _ptr(v1), _ptr(v2), _ptr(vn), S_cap, int(S_kv),
+                                         float(scale), _ptr(out), _stream_handle(stream)), "kvq_rvq_attend_noalloc")
 
 
 def attend(q, kcache, vcache, cbk: Codebooks, cbv: Codebooks, S_kv: int, scale=None, stream=None):

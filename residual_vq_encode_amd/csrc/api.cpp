@@ -15,7 +15,10 @@ hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipSt
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream);
 hipError_t launch_qjl(const QjlArgs& a, int d, int m, hipStream_t stream);
+hipError_t attend_scratch(void** ptr);
 }  // namespace kvq
+
+static_assert(kvq::kAttendScratchBytes == KVQ_ATTEND_SCRATCH_BYTES, "the header states the scratch size");
 
 namespace {
 
@@ -429,12 +432,16 @@ extern "C" kvq_status kvq_rvq_attend_workspace_size(int32_t d, int32_t bits, int
   return KVQ_OK;
 }
 
-extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
-                                     int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, const uint32_t* k_packed1,
-                                     const uint32_t* k_packed2, const float* k_norms, const uint32_t* v_packed1,
-                                     const uint32_t* v_packed2, const float* v_norms, int64_t S_cap, int64_t S_kv,
-                                     float scale, void* workspace, int64_t workspace_bytes, uint16_t* out,
-                                     void* stream) {
+namespace {
+
+// The attention's checks and launch. With use_scratch the partial records go to the
+// library's device scratch (looked up after every host check has passed, so a rejected
+// call still touches no device state) and workspace / workspace_bytes are ignored.
+kvq_status attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q, int64_t B, int64_t Hq,
+                  int64_t Sq, int64_t Hkv, const uint32_t* k_packed1, const uint32_t* k_packed2, const float* k_norms,
+                  const uint32_t* v_packed1, const uint32_t* v_packed2, const float* v_norms, int64_t S_cap,
+                  int64_t S_kv, float scale, void* workspace, int64_t workspace_bytes, bool use_scratch, uint16_t* out,
+                  void* stream) {
   kvq_status st = check_codebooks(cbk);
   if (st != KVQ_OK) return st;
   st = check_codebooks(cbv);
@@ -457,13 +464,18 @@ extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codeboo
   if (p.n_q == 0) return KVQ_OK;
   if (!std::isfinite(scale)) return KVQ_ERR_ARG;
   if (q == nullptr || k_packed1 == nullptr || k_packed2 == nullptr || k_norms == nullptr || v_packed1 == nullptr ||
-      v_packed2 == nullptr || v_norms == nullptr || workspace == nullptr || out == nullptr)
+      v_packed2 == nullptr || v_norms == nullptr || (!use_scratch && workspace == nullptr) || out == nullptr)
     return KVQ_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 16) || !aligned(k_packed1, 16) ||
+  if (!aligned(q, 16) || !aligned(out, 16) || (!use_scratch && !aligned(workspace, 16)) || !aligned(k_packed1, 16) ||
       !aligned(k_packed2, 16) || !aligned(v_packed1, 16) || !aligned(v_packed2, 16) || !aligned(k_norms, 4) ||
       !aligned(v_norms, 4))
     return KVQ_ERR_ALIGN;
-  if (workspace_bytes < p.ws_bytes) return KVQ_ERR_RANGE;
+  if (use_scratch) {
+    if (p.ws_bytes > kvq::kAttendScratchBytes) return KVQ_ERR_RANGE;
+    if (kvq::attend_scratch(&workspace) != hipSuccess) return KVQ_ERR_DEVICE;
+  } else if (workspace_bytes < p.ws_bytes) {
+    return KVQ_ERR_RANGE;
+  }
 
   AttendArgs a;
   a.q = q;
@@ -498,4 +510,26 @@ extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codeboo
   std::memcpy(a.vsign, cbv->sign_bits, sizeof(a.vsign));
   const hipError_t e = kvq::launch_attend(a, cbk->d, cbk->bits, p.nqw, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_rvq_attend(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
+                                     int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv, const uint32_t* k_packed1,
+                                     const uint32_t* k_packed2, const float* k_norms, const uint32_t* v_packed1,
+                                     const uint32_t* v_packed2, const float* v_norms, int64_t S_cap, int64_t S_kv,
+                                     float scale, void* workspace, int64_t workspace_bytes, uint16_t* out,
+                                     void* stream) {
+  return attend(cbk, cbv, q, B, Hq, Sq, Hkv, k_packed1, k_packed2, k_norms, v_packed1, v_packed2, v_norms, S_cap, S_kv,
+                scale, workspace, workspace_bytes, false, out, stream);
+}
+
+extern "C" kvq_status kvq_rvq_attend_noalloc(const kvq_codebooks* cbk, const kvq_codebooks* cbv, const uint16_t* q,
+                                             int64_t B, int64_t Hq, int64_t Sq, int64_t Hkv,
+                                             const uint32_t* k_packed1, const uint32_t* k_packed2,
+                                             const float* k_norms, const uint32_t* v_packed1,
+                                             const uint32_t* v_packed2, const float* v_norms, int64_t S_cap,
+                                             int64_t S_kv, float scale, uint16_t* out, void* stream) {
+  return attend(cbk, cbv, q, B, Hq, Sq, Hkv, k_packed1, k_packed2, k_norms, v_packed1, v_packed2, v_norms, S_cap, S_kv,
+                scale, nullptr, 0, true, out, stream);
 }

@@ -23,6 +23,7 @@
 // single v_exp_f32 instructions.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cfloat>
 #include <climits>
 
@@ -979,6 +980,37 @@ static auto attend_fn(int bits, int nqw) -> hipError_t (*)(const AttendArgs&, hi
 // Launcher used by api.cpp: both kernels on `stream`, the combine after the partials.
 // nqw: query vectors per wave: 16 selects the matrix-core pass (d = 64 or 128, b = 1, 2 or
 // 4, d b >= 128); else 1, 2 or 4 (a divisor of group * Sq; 1 for d = 1024).
+// ------------------------------------------------------------------------------ scratch
+
+// Device scratch of the allocation-free attention entry point (kvq_rvq_attend_noalloc): the
+// per-(query vector, chunk) records of the partial pass live here instead of in a caller's
+// workspace. One copy per device, held from the library's load until the process ends. The
+// partial pass rewrites every record the combine pass reads, so nothing needs clearing
+// between calls; calls that overlap on one device share it and race.
+static __device__ __align__(256) float scratch[kAttendScratchBytes / sizeof(float)];
+
+// Device address of this device's scratch array, looked up with the device current at the
+// first call on each device and kept (a host-side use of the array's name would be a
+// host-side stand-in, not its device address). Two threads racing on the first call both
+// store the same address.
+hipError_t attend_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_attend(const AttendArgs& a, int d, int bits, int nqw, hipStream_t stream) {
   hipError_t (*f)(const AttendArgs&, hipStream_t) = nullptr;
   switch (d) {

@@ -98,6 +98,11 @@ namespace kvq {
 
 // Attention over a packed cache (attend.hip): scores of the query against every cached key
 // and the softmax-weighted sum of the cached values, both caches read packed.
+// Bytes of device scratch behind kvq_rvq_attend_noalloc: 32 MiB holds the partial records
+// of a decode step (a few query positions) at every supported d up to 16 query heads per
+// key/value head.
+constexpr int64_t kAttendScratchBytes = int64_t(32) << 20;
+
 struct AttendArgs {
   const uint16_t* q;                // fp16 [B, Hq, Sq, d]
   const uint32_t* k1;               // key cache streams [B, Hkv, S_cap, n_words]

@@ -377,6 +377,39 @@ void test_tile_limit() {
   CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 1, 1, 16 * imax + 1, 0, 16 * imax + 1, x, nullptr) == KVQ_ERR_RANGE);
 }
 
+// The allocation-free attention: the same checks as kvq_rvq_attend, all on the host before
+// the scratch is looked up; plans beyond the scratch are refused with KVQ_ERR_RANGE; a good
+// call launches with the scratch address as its workspace.
+void test_attend_noalloc() {
+  kvq_codebooks ck, cv;
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &ck) == KVQ_OK);
+  CHECK(kvq_build_codebooks(128, 2, nullptr, &cv) == KVQ_OK);
+  uint16_t* q = fake<uint16_t>(0x10000);
+  uint16_t* out = fake<uint16_t>(0x11000);
+  uint32_t* p1 = fake<uint32_t>(0x20000);
+  uint32_t* p2 = fake<uint32_t>(0x30000);
+  float* nr = fake<float>(0x40000);
+  kvq::g_stub = kvq::StubLog{};
+  CHECK(kvq_rvq_attend_noalloc(&ck, &cv, q, 1, 32, 1, 8, p1, p2, nr, p1, p2, nr, 32768, 32768, 0.1f, out, nullptr) ==
+        KVQ_OK);
+  CHECK(kvq::g_stub.attend_calls == 1 && kvq::g_stub.scratch_lookups == 1);
+  CHECK(kvq::g_stub.att.ws == reinterpret_cast<float*>(uintptr_t(0x7000000)));
+  // 131072 query vectors of one position each need 131072 x 132 x 4 bytes (69 MB) of records
+  int64_t need = 0;
+  CHECK(kvq_rvq_attend_workspace_size(128, 2, 1, 32, 4096, 8, 4096, &need) == KVQ_OK);
+  CHECK(need > KVQ_ATTEND_SCRATCH_BYTES);
+  CHECK(kvq_rvq_attend_noalloc(&ck, &cv, q, 1, 32, 4096, 8, p1, p2, nr, p1, p2, nr, 4096, 4096, 0.1f, out, nullptr) ==
+        KVQ_ERR_RANGE);
+  // argument errors come before the lookup
+  CHECK(kvq_rvq_attend_noalloc(&ck, &cv, q, 1, 32, 1, 8, p1, p2, nr, p1, p2, nr, 4096, 4096, 0.1f, nullptr, nullptr) ==
+        KVQ_ERR_ARG);
+  CHECK(kvq_rvq_attend_noalloc(&ck, &cv, q, 1, 32, 1, 7, p1, p2, nr, p1, p2, nr, 4096, 4096, 0.1f, out, nullptr) ==
+        KVQ_ERR_SHAPE);
+  CHECK(kvq_rvq_attend_noalloc(&ck, &cv, fake<uint16_t>(0x10002), 1, 32, 1, 8, p1, p2, nr, p1, p2, nr, 4096, 4096,
+                               0.1f, out, nullptr) == KVQ_ERR_ALIGN);
+  CHECK(kvq::g_stub.attend_calls == 1 && kvq::g_stub.scratch_lookups == 1);
+}
+
 // ------------------------------------------------------------------------------ QJL
 
 void test_qjl() {
@@ -489,6 +522,7 @@ int main() {
   test_bucket_tables();
   test_qjl();
   test_attend();
+  test_attend_noalloc();
   test_status_text();
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);

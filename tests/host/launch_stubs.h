@@ -7,7 +7,7 @@
 namespace kvq {
 
 struct StubLog {
-  int encode_calls = 0, decode_calls = 0, attend_calls = 0, qjl_calls = 0;
+  int encode_calls = 0, decode_calls = 0, attend_calls = 0, qjl_calls = 0, scratch_lookups = 0;
   int d = 0, bits = 0, stages = 0, nqw = 0, m = 0;
   EncodeArgs enc{};
   DecodeArgs dec{};

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol():
     lib = kvq.load()
     names = _declared_functions()
     assert names == ["kvq_build_codebooks", "kvq_mse_encode_pack", "kvq_mse_unpack_decode", "kvq_qjl_encode_pack",
-                     "kvq_qjl_supported", "kvq_rabitq_encode_pack", "kvq_rvq_attend", "kvq_rvq_attend_workspace_size",
+                     "kvq_qjl_supported", "kvq_rabitq_encode_pack", "kvq_rvq_attend", "kvq_rvq_attend_noalloc",
+                     "kvq_rvq_attend_workspace_size",
                      "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_status_str"]
     for n in names:
         assert hasattr(lib, n), n
