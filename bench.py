@@ -4,19 +4,23 @@
 
 One step is one pass of the whole path over one synthetic layer: encode+pack of a
 [1, 32, 8192, 128] fp16 key tensor at b = 2 bits per stage (4 outlier channels, random
-signs), then the unpack+decode of the packed result. Inputs are resident in HBM before
+signs), then an unpack+decode of a tensor of the same size. Inputs are resident in HBM before
 timing starts and rotate through a pool of distinct tensors (and distinct output buffers)
-larger than twice the 256 MB last-level cache, so every encode streams its input from HBM.
+larger than twice the 256 MB last-level cache, so every encode streams its input from HBM;
+the decodes read their own pool of packed caches (also more than twice that cache), written
+before the timed region.
 
-Timing: the K steps run in blocks of 10 on one stream: 10 encode launches back to back,
-then the 10 matching decode launches, then the next block. HIP events recorded on that
-stream bracket every block, and the timed region is bracketed by device synchronisation on
-both sides. The average encode launch duration is the sum of the encode blocks' spans over
-K (it includes the gaps between back-to-back launches); the per-block averages give p10,
-p50, p90 and an A/A noise floor (even against odd blocks). `value` is encode+pack throughput: algorithmic bytes per launch
-(fp16 bytes in + packed bytes out; the 4-byte norms are reported separately, not counted)
-over that average, checked against the 8 TB/s HBM peak in `roofline`. `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same tensor.
+Timing: the K steps' encodes run first, then their decodes, on one stream, in blocks of
+min(10, K / 4) back-to-back launches. HIP events recorded on that stream bracket every
+block, and the timed region is bracketed by device synchronisation on both sides. The average encode launch duration is the sum of the
+encode blocks' spans over K (it includes the gaps between back-to-back launches); the
+per-block averages give p10, p50, p90 and an A/A noise floor (even against odd blocks).
+`value` is encode+pack throughput: algorithmic bytes per launch (fp16 bytes in + packed
+bytes out; the 4-byte norms are reported separately, not counted) over that average,
+checked against the 8 TB/s HBM peak in `roofline`. Before timing, the line records whether
+any other process holds the GPU and how busy it is (`gpu_idle_check`), and which GPU, ROCm
+and host it ran on (`host`). `cpu_baseline` is the CPU oracle timed on a bounded sample of
+the same tensor, with its BLAS threads and with one thread.
 
 `roofline.traffic` (measured HBM bytes per encode launch) comes from
 profiles/traffic_<workload>.json, which `--traffic-from FETCH.csv WRITE.csv COPY_BYTES`
@@ -39,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 COPY_BYTES = 1 << 30  # --copy-calibration: one plain device copy reads and writes this many bytes
 WORKLOADS = {
     # name: (tensor preset in synth.WORKLOADS, bits, pool size, stages)
@@ -66,22 +71,34 @@ ATTEND_WORKLOADS = {"attend_decode": {"B": 1, "Hq": 32, "Hkv": 8, "Sq": 1, "S_kv
                                       "pool": 16}}
 
 
-BLOCK = 10  # launches per timed block
+def block_size(steps: int) -> int:
+    """Launches per timed block: 10, or fewer so that even a short run has 4 blocks (the A/A
+    noise floor compares even and odd blocks)."""
+    return max(1, min(10, steps // 4))
 
 
-def spread(per_block):
+def spread(per_block, block):
     """p10 / p50 / p90 of per-launch block averages (us), and the A/A noise floor: the
     relative gap between the medians of the even and the odd blocks (the same kernel on the
     same pool, interleaved in time)."""
     import numpy as np
     v = np.asarray(per_block, dtype=np.float64)
-    out = {"blocks": int(v.size), "launches_per_block": BLOCK}
+    out = {"blocks": int(v.size), "launches_per_block": block}
     for q in (10, 50, 90):
         out[f"p{q}"] = round(float(np.percentile(v, q)), 3)
     if v.size >= 4:
         a, b = float(np.median(v[0::2])), float(np.median(v[1::2]))
         out["aa_noise"] = round(abs(a - b) / float(np.median(v)), 4)
     return out
+
+
+def encode_kernel_name(D: int, bits: int, contig: bool, stages: int) -> str:
+    """The encode kernel libkvq launches for this shape (the matrix-core kernel covers D = 128
+    at 1, 2 and 4 bits, the butterfly kernel everything else)."""
+    c = "true" if contig else "false"
+    if D == 128 and bits != 3:
+        return f"kvq::encode_mx_kernel<{bits}, {c}, {stages}>"
+    return f"kvq::encode_kernel<{D}, {bits}, {c}, {stages}>"
 
 
 def kernel_source_hash() -> str:
@@ -91,8 +108,122 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def host_info() -> dict:
+    """The GPU, the ROCm stack and the host the numbers come from."""
+    import torch
+    info = {"host_cores": os.cpu_count()}
+    try:
+        info["affinity_cores"] = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        info["gpu"] = pr.name
+        info["gpu_arch"] = getattr(pr, "gcnArchName", "")
+        info["gpu_cus"] = pr.multi_processor_count
+    except Exception:
+        pass
+    info["torch_hip"] = torch.version.hip
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except Exception:
+        pass
+    return info
+
+
+def gpu_idle_check() -> dict:
+    """Is anything else using the GPU? Other processes holding the device (their entries under
+    /sys/class/kfd/kfd/proc) and the device's busy percentage, sampled a few times before the
+    timed region. A busy GPU makes every timing below it wrong, so the line says so."""
+    out = {}
+    try:
+        pids = [int(p) for p in os.listdir("/sys/class/kfd/kfd/proc") if p.isdigit()]
+        out["other_gpu_processes"] = sorted(p for p in pids if p != os.getpid())
+        out["source"] = "/sys/class/kfd/kfd/proc"
+    except Exception:
+        try:
+            import re
+            import subprocess
+            r = subprocess.run(["rocm-smi", "--showpids"], capture_output=True, text=True, timeout=20)
+            pids = [int(m) for m in re.findall(r"^\s*(\d+)\s+\S+", r.stdout, re.M)]
+            out["other_gpu_processes"] = sorted(p for p in pids if p != os.getpid()) if r.returncode == 0 else None
+            out["source"] = "rocm-smi --showpids"
+        except Exception as e:
+            out["other_gpu_processes"] = None
+            out["source"] = f"unavailable ({type(e).__name__})"
+    busy = []
+    try:
+        import glob
+        files = sorted(glob.glob("/sys/class/drm/card*/device/gpu_busy_percent"))
+        for _ in range(5):
+            busy.append(max(int(open(f).read()) for f in files))
+            time.sleep(0.02)
+    except Exception:
+        busy = []
+    out["gpu_busy_percent_samples"] = busy or None
+    others = out["other_gpu_processes"]
+    out["idle"] = (others is not None and len(others) == 0) and (not busy or max(busy) <= 10)
+    return out
+
+
+def stream_reference(in_bytes: int, out_bytes: int, reps: int = 50) -> dict:
+    """A plain device-to-device copy (hipMemcpyAsync) moving the encode's total byte count:
+    (in + out) / 2 bytes read and as many written, over a pool of distinct buffers larger than
+    twice the last-level cache, back to back under events. A reference for what the machine
+    streams without any arithmetic, next to the encode's own rate."""
+    import torch
+    dev = torch.device("cuda:0")
+    half = ((in_bytes + out_bytes) // 2) // 16 * 16
+    pool = max(2, -(-(2 * LLC_BYTES + 1) // (2 * half)))
+    src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(pool)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(pool)]
+    for i in range(10):
+        dst[i % pool].copy_(src[i % pool])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst[i % pool].copy_(src[i % pool])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_us": round(us, 3), "copy_GBps": round(2 * half / us / 1e3, 1), "bytes_moved": 2 * half,
+            "pool": pool, "kernel": "device-to-device copy (hipMemcpyAsync) of the same total bytes"}
+
+
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        return max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    except Exception:
+        return 1
+
+
+def one_thread(fn):
+    """Run fn with the BLAS thread pools held to one thread (the oracle's other steps are
+    single-threaded numpy already)."""
+    try:
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            return fn()
+    except ImportError:
+        return fn()
+
+
 def cpu_baseline(spec, signs, bits, stages: int = 2, target_s: float = 15.0) -> dict:
-    """The oracle, as it stands, on a contiguous sample of the workload's first tensor."""
+    """The oracle, as it stands, on a contiguous sample of the workload's first tensor: with
+    numpy's BLAS thread pool as the process has it (only the Hadamard products use it; the
+    nearest-centroid search and the packing are single-threaded numpy), and again held to
+    one thread on a smaller sample."""
     import numpy as np
     import synth
     from oracle import codebooks as ocb
@@ -111,15 +242,22 @@ def cpu_baseline(spec, signs, bits, stages: int = 2, target_s: float = 15.0) -> 
     run(x, s, t)
     dt = time.perf_counter() - t0
     nw = -(-spec.D // (32 // bits))
-    nbytes = n * (spec.D * 2 + stages * nw * 4)
-    try:
-        import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
-    except Exception:
-        cores = os.cpu_count()
-    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {spec.rows} vectors of the workload tensor, encode+pack, "
-                      f"{dt:.1f} s wall, numpy float64 oracle on {cores} BLAS threads"}
+    per_vec = spec.D * 2 + stages * nw * 4
+    threads = blas_threads()
+    n1 = min(n, 65536)
+    x1 = x[:n1]
+    t0 = time.perf_counter()
+    one_thread(lambda: run(x1, s, t))
+    dt1 = time.perf_counter() - t0
+    info = host_info()
+    return {"value": round(n * per_vec / dt / 1e9, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {spec.rows} vectors of the workload tensor, encode+pack, {dt:.1f} s wall; "
+                      f"numpy float64 oracle (not an optimised CPU codec), its Hadamard products on "
+                      f"{threads} BLAS threads, the rest on one",
+            "one_thread": {"value": round(n1 * per_vec / dt1 / 1e9, 6), "unit": "GB/s",
+                           "sample": f"first {n1} vectors, {dt1:.1f} s wall, BLAS held to one thread"},
+            "host_cores": info.get("host_cores"), "affinity_cores": info.get("affinity_cores"),
+            "cpu_model": info.get("cpu_model")}
 
 
 def traffic_for(workload: str):
@@ -150,7 +288,7 @@ def traffic_from(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int)
     rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "copy_bytes": copy_bytes}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = _counter_rows(path, counter)
-        enc = [v for k, v in rows if "encode_kernel" in k]
+        enc = [v for k, v in rows if "encode_kernel" in k or "encode_mx_kernel" in k]
         copy = [v for k, v in rows if "copy" in k.lower()]
         copy = [v for v in copy if v > copy_bytes / 4]  # the 1 GiB copies, not small helper kernels
         if not enc or not copy:
@@ -175,6 +313,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run plain {COPY_BYTES >> 30} GiB device copies (the counter-scaling reference)")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="also time a plain device copy moving the encode's total byte count")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
@@ -209,6 +349,7 @@ def main() -> int:
         return bench_attend(args)
     if args.workload in SIGN_WORKLOADS:
         return bench_signcodes(args)
+    idle = gpu_idle_check()  # before this process puts any work on the GPU
     wname, bits, pool_default, stages = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wname]
     spec = w.tensors[0]
@@ -228,6 +369,14 @@ def main() -> int:
     ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(P)]
     outs = [torch.empty((B, H, S, D), dtype=torch.float16, device=dev) for _ in range(P)]
     stream = torch.cuda.current_stream()
+    # The decodes read their own pool of packed caches, more than twice the 256 MB last-level
+    # cache, each written by an encode before the timed region: a decode's input then comes
+    # from HBM, not from the caches the encode blocks have just written.
+    packed_bytes = B * H * S * (stages * nw * 4 + 4)
+    PD = min(64, max(P, -(-(2 * LLC_BYTES + 1) // packed_bytes)))
+    dq1 = [torch.empty_like(p1s[0]) for _ in range(PD)]
+    dq2 = [torch.empty_like(p1s[0]) for _ in range(PD)] if stages == 2 else None
+    dqn = [torch.empty_like(ns[0]) for _ in range(PD)]
 
     if args.copy_calibration:
         a = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev)
@@ -237,45 +386,55 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    if stages == 2:
-        def enc(j):
-            kvq.kvq_rvq_encode_pack(cb, xs[j], p1s[j], p2s[j], ns[j], 0, stream)
+    # Launches are prepared once (arguments checked and marshalled by the binding), so the
+    # timed loop issues them as fast as the host can call the C ABI and the events measure
+    # the GPU rather than per-call Python checks.
+    encs = [kvq.prepare_encode(cb, xs[j], p1s[j], p2s[j] if stages == 2 else None, ns[j], 0, stream, stages)
+            for j in range(P)]
+    decs = [kvq.prepare_decode(cb, dq1[k], dq2[k] if stages == 2 else None, dqn[k], outs[k % P], 0, stream, stages)
+            for k in range(PD)]
+    for k in range(PD):
+        kvq.prepare_encode(cb, xs[k % P], dq1[k], dq2[k] if stages == 2 else None, dqn[k], 0, stream, stages)()
 
-        def dec(j):
-            kvq.kvq_rvq_unpack_decode(cb, p1s[j], p2s[j], ns[j], outs[j], 0, stream)
-    else:
-        def enc(j):
-            kvq.kvq_mse_encode_pack(cb, xs[j], p1s[j], ns[j], 0, stream)
+    def enc(j):
+        encs[j]()
 
-        def dec(j):
-            kvq.kvq_mse_unpack_decode(cb, p1s[j], ns[j], outs[j], 0, stream)
+    def dec(j):
+        decs[j % PD]()
 
+    # warm-up: the decodes first, then the encodes, so the timed encodes follow encodes
+    for i in range(args.warmup):
+        dec(i)
     for i in range(args.warmup):
         enc(i % P)
-        dec(i % P)
     torch.cuda.synchronize()
 
-    # The K steps run in blocks: a block of encodes back to back, then the same tensors'
-    # decodes, the two kernels taking turns. Events between the blocks give per-block
-    # averages (their spread, and an A/A noise floor from alternate encode blocks).
+    # The K steps' encodes run first, then their decodes, each in blocks of back-to-back
+    # launches with events between the blocks (per-block averages give the spread and an A/A
+    # noise floor from alternate blocks). Grouping the kernels keeps each in its own steady
+    # state: a decode block writes ten 67 MB outputs, and encodes interleaved with it would
+    # share the HBM with the write-back of those bytes.
     K = args.steps
+    BLOCK = block_size(K)
     blocks = [(a, min(a + BLOCK, K)) for a in range(0, K, BLOCK)]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(blocks) + 1)]
+    nb = len(blocks)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nb + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev[0].record(stream)
     for bi, (a, b) in enumerate(blocks):
         for i in range(a, b):
             enc((args.warmup + i) % P)
-        ev[2 * bi + 1].record(stream)
+        ev[bi + 1].record(stream)
+    for bi, (a, b) in enumerate(blocks):
         for i in range(a, b):
-            dec((args.warmup + i) % P)
-        ev[2 * bi + 2].record(stream)
+            dec(args.warmup + i)
+        ev[nb + bi + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    enc_blk = [ev[2 * bi].elapsed_time(ev[2 * bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
-    dec_blk = [ev[2 * bi + 1].elapsed_time(ev[2 * bi + 2]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+    enc_blk = [ev[bi].elapsed_time(ev[bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+    dec_blk = [ev[nb + bi].elapsed_time(ev[nb + bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
     enc_us = sum(t * (b - a) for t, (a, b) in zip(enc_blk, blocks)) / K
     dec_us = sum(t * (b - a) for t, (a, b) in zip(dec_blk, blocks)) / K
     total_ms = ev[0].elapsed_time(ev[-1])
@@ -329,17 +488,24 @@ def main() -> int:
         "tokens_per_s": round(B * S / (enc_us * 1e-6), 1),
         "head_vectors_per_s": round(n_vec / (enc_us * 1e-6), 1),
         "encode_us_per_launch": round(enc_us, 3),
-        "encode_us_blocks": spread(enc_blk),
+        "encode_us_blocks": spread(enc_blk, BLOCK),
         "decode_us_per_launch": round(dec_us, 3),
-        "decode_us_blocks": spread(dec_blk),
+        "decode_us_blocks": spread(dec_blk, BLOCK),
         "decode_GBps": round(dec_gbps, 1),
+        "decode_input_pool": {"caches": PD, "bytes": PD * packed_bytes,
+                              "note": "decodes read packed caches written before the timed region, "
+                                      "more than twice the last-level cache"},
         "norm_bytes_per_launch_not_counted": n_vec * 4,
         "wall_s_timed_region": round(wall, 4),
         "parity_recheck": {"vectors": int(len(idx)), "flip_fraction": rep.flip_fraction, "ok": bool(parity_ok)},
         "roofline": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(enc_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": enc_bytes, "kernel": f"kvq::encode_kernel<{D}, {bits}, true, {stages}>"},
+                     "algorithmic_bytes_per_launch": enc_bytes, "kernel": encode_kernel_name(D, bits, True, stages)},
+        "gpu_idle_check": idle,
+        "host": host_info(),
     }
+    if args.stream_reference:
+        result["stream_reference"] = stream_reference(n_vec * D * 2, n_vec * stages * nw * 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, signs, bits, stages)
     print(json.dumps(result), flush=True)
@@ -377,7 +543,7 @@ def bench_signcodes(args) -> int:
 
         def enc(j):
             kvq.kvq_rabitq_encode_pack(cb, xs[j], ps[j], ns[j], 0, stream)
-        out_bytes, norm_bytes, kname = nw * 4, 4, f"kvq::encode_kernel<{D}, 1, true, 0>"
+        out_bytes, norm_bytes, kname = nw * 4, 4, encode_kernel_name(D, 1, True, 0)
     else:
         sk = synth.tensor(synth.TensorSpec(1, 1, m, D, "gauss", 707), device=dev).reshape(m, D).contiguous()
         nw = m // 32
@@ -391,6 +557,7 @@ def bench_signcodes(args) -> int:
     for i in range(args.warmup):
         enc(i % P)
     torch.cuda.synchronize()
+    idle = gpu_idle_check()
     K = args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -426,14 +593,11 @@ def bench_signcodes(args) -> int:
     dt_oracle = time.perf_counter() - t0
     frac = float(diff.mean())
     ok = in_window and norm_ok and frac <= max(1e-6, 1.0 / diff.size)
-    try:
-        import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
-    except Exception:
-        cores = os.cpu_count()
+    cores = blas_threads()
     result = {
         "metric": "encode+pack GB/s (fp16 in + packed out) and % of HBM peak; tokens/sec",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "gpu_idle_check": idle, "host": host_info(),
         "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded counter-based generator; no dataset)",
         "config": {"workload": f"{args.workload}: {w.note.split('; b=')[0]}; " + (
@@ -498,6 +662,7 @@ def bench_attend(args) -> int:
     for i in range(args.warmup):
         run(i % P)
     torch.cuda.synchronize()
+    idle = gpu_idle_check()
     K = args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -535,11 +700,7 @@ def bench_attend(args) -> int:
     got = out.cpu().numpy().astype(np.float64)
     rowmax = np.max(np.abs(want), axis=-1, keepdims=True)
     ok = bool(np.all(np.abs(got - want) <= 2.0 ** -10 * np.abs(want) + 1e-3 * rowmax))
-    try:
-        import threadpoolctl
-        cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
-    except Exception:
-        cores = os.cpu_count()
+    cores = blas_threads()
     result = {
         "metric": "attention over the packed cache: packed key+value bytes read per second (GB/s); decode steps/s",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -547,7 +708,7 @@ def bench_attend(args) -> int:
         "dtype": "f32", "data": "synthetic (seeded counter-based generator; no dataset)",
         "config": {"workload": f"{args.workload}: one decode step, q [{B},{Hq},{Sq},{D}] over packed K and V "
                                f"[{B},{Hkv},{S},{D}] b={bits}", "bits": bits, "pool": P},
-        "us_per_step": round(us, 3), "steps_per_s": round(1e6 / us, 1),
+        "us_per_step": round(us, 3), "steps_per_s": round(1e6 / us, 1), "gpu_idle_check": idle, "host": host_info(),
         "parity_recheck": {"query_vectors": B * Hq * Sq, "ok": ok,
                            "max_rel_err": float(np.max(np.abs(got - want) / np.maximum(rowmax, 1e-30)))},
         "wall_s_timed_region": round(wall, 4),
@@ -592,16 +753,25 @@ def bench_append(args) -> int:
     steps = [synth.step_rows(spec, t, device=dev).contiguous() for t in range(K)]
     stream = torch.cuda.current_stream()
 
+    # one prepared launch per step and stream (arguments checked and marshalled once)
+    launches = {}
+
     def run_all():
         st = torch.cuda.current_stream()
-        for t in range(K):
-            kvq.kvq_rvq_encode_pack(cb, steps[t], p1, p2, nrm, t, st)
+        key = st.cuda_stream
+        if key not in launches:
+            launches[key] = [kvq.prepare_encode(cb, steps[t], p1, p2, nrm, t, st) for t in range(K)]
+        for launch in launches[key]:
+            launch()
 
     for t in range(min(args.warmup, K)):
         kvq.kvq_rvq_encode_pack(cb, steps[t], p1, p2, nrm, t, stream)
     torch.cuda.synchronize()
+    idle = gpu_idle_check()
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run_all()  # prepares this stream's launches (and runs the steps once, untimed)
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
     run_all()
@@ -659,6 +829,7 @@ def bench_append(args) -> int:
         "data": "synthetic (seeded counter-based generator; no dataset)",
         "config": {"workload": f"decode_append: {K} steps of [{B},{H},1,{D}] appended into S_cap={S_cap} caches; b={bits}",
                    "bits": bits, "timing": "one captured graph of the K launches, replayed"},
+        "gpu_idle_check": idle, "host": host_info(),
         "us_per_step_graph": round(graph_us, 3),
         "us_per_step_eager": round(eager_us, 3),
         "wall_s_timed_region": round(wall, 4),
@@ -667,7 +838,7 @@ def bench_append(args) -> int:
         "roofline": {"bound": "launch", "achieved": round(step_bytes / (graph_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(step_bytes / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 5),
                      "traffic": None, "algorithmic_bytes_per_launch": step_bytes,
-                     "kernel": f"kvq::encode_kernel<{D}, {bits}, false, 2>"},
+                     "kernel": encode_kernel_name(D, bits, False, 2)},
     }
     if not args.no_cpu_baseline:
         n_s = min(K, 20)
@@ -675,11 +846,7 @@ def bench_append(args) -> int:
         t0 = time.perf_counter()
         rvq.encode(x, signs, t_tab)
         dt = time.perf_counter() - t0
-        try:
-            import threadpoolctl
-            cores = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
-        except Exception:
-            cores = os.cpu_count()
+        cores = blas_threads()
         result["cpu_baseline"] = {"value": round(n_s * B / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                                   "sample": f"the first {n_s} steps ({n_s * B * H} vectors), encode+pack, {dt:.2f} s wall, "
                                             f"numpy float64 oracle"}

@@ -29,7 +29,7 @@ __all__ = [
     "kvq_rvq_encode_pack", "kvq_rvq_unpack_decode", "kvq_mse_encode_pack", "kvq_mse_unpack_decode",
     "kvq_rvq_attend", "kvq_rvq_attend_workspace_size", "kvq_rvq_attend_noalloc", "ATTEND_SCRATCH_BYTES", "kvq_rabitq_encode_pack", "kvq_qjl_encode_pack",
     "kvq_qjl_supported", "kvq_status_str", "encode", "decode", "encode_mse", "decode_mse", "encode_rabitq",
-    "encode_qjl", "attend", "n_words",
+    "encode_qjl", "attend", "n_words", "PreparedLaunch", "prepare_encode", "prepare_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -188,6 +188,71 @@ def kvq_rvq_encode_pack(cb: Codebooks, x, packed1, packed2, norms, s_offset: int
     _check(load().kvq_rvq_encode_pack(ctypes.byref(cb), _ptr(x), B, H, S, _ptr(packed1), _ptr(packed2),
                                       _ptr(norms), S_cap, int(s_offset), _stream_handle(stream)),
            "kvq_rvq_encode_pack")
+
+
+class PreparedLaunch:
+    """One C ABI call with its arguments validated and marshalled once (prepare_encode,
+    prepare_decode): calling it only makes the C call and checks the status, so a loop of
+    launches is not held up by Python-side checks. The tensors it was prepared with must stay
+    alive and keep their storage."""
+    __slots__ = ("_fn", "_args", "_what", "_keep")
+
+    def __init__(self, fn, args, what, keep):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != 0:
+            raise KvqError(status, self._what)
+
+
+def prepare_encode(cb: Codebooks, x, packed1, packed2, norms, s_offset: int = 0, stream=None,
+                   stages: int = 2) -> PreparedLaunch:
+    """kvq_rvq_encode_pack (stages=2) or kvq_mse_encode_pack (stages=1, packed2 ignored) on
+    these tensors, validated as by those calls, as a PreparedLaunch."""
+    import torch
+    _require_cuda(x, packed1, packed2 if stages == 2 else None, norms)
+    if x.dtype != torch.float16 or x.dim() != 4 or not x.is_contiguous() or x.shape[3] != cb.d:
+        raise ValueError("x must be a contiguous fp16 [B, H, S, d] tensor matching the codebooks")
+    B, H, S, _ = x.shape
+    S_cap = packed1.shape[2]
+    for name, t in (("packed1", packed1),) + ((("packed2", packed2),) if stages == 2 else ()):
+        _check_stream(cb, name, t, B, H, S_cap)
+    if tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32 or not norms.is_contiguous():
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    cbp = ctypes.pointer(cb)
+    lib = load()
+    if stages == 2:
+        args = (cbp, _ptr(x), B, H, S, _ptr(packed1), _ptr(packed2), _ptr(norms), S_cap, int(s_offset),
+                _stream_handle(stream))
+        return PreparedLaunch(lib.kvq_rvq_encode_pack, args, "kvq_rvq_encode_pack", (cb, x, packed1, packed2, norms))
+    args = (cbp, _ptr(x), B, H, S, _ptr(packed1), _ptr(norms), S_cap, int(s_offset), _stream_handle(stream))
+    return PreparedLaunch(lib.kvq_mse_encode_pack, args, "kvq_mse_encode_pack", (cb, x, packed1, norms))
+
+
+def prepare_decode(cb: Codebooks, packed1, packed2, norms, out, s_offset: int = 0, stream=None,
+                   stages: int = 2) -> PreparedLaunch:
+    """kvq_rvq_unpack_decode (stages=2) or kvq_mse_unpack_decode (stages=1, packed2 ignored)
+    into out, validated as by those calls, as a PreparedLaunch."""
+    import torch
+    _require_cuda(packed1, packed2 if stages == 2 else None, norms, out)
+    if out.dtype != torch.float16 or out.dim() != 4 or not out.is_contiguous() or out.shape[3] != cb.d:
+        raise ValueError("out must be a contiguous fp16 [B, H, S, d] tensor")
+    B, H, S, _ = out.shape
+    S_cap = packed1.shape[2]
+    for name, t in (("packed1", packed1),) + ((("packed2", packed2),) if stages == 2 else ()):
+        _check_stream(cb, name, t, B, H, S_cap)
+    if norms is not None and (tuple(norms.shape) != (B, H, S_cap) or norms.dtype != torch.float32
+                              or not norms.is_contiguous()):
+        raise ValueError(f"norms must be contiguous float32 {(B, H, S_cap)}")
+    cbp = ctypes.pointer(cb)
+    lib = load()
+    if stages == 2:
+        args = (cbp, _ptr(packed1), _ptr(packed2), _ptr(norms), B, H, S_cap, int(s_offset), S, _ptr(out),
+                _stream_handle(stream))
+        return PreparedLaunch(lib.kvq_rvq_unpack_decode, args, "kvq_rvq_unpack_decode", (cb, packed1, packed2, norms, out))
+    args = (cbp, _ptr(packed1), _ptr(norms), B, H, S_cap, int(s_offset), S, _ptr(out), _stream_handle(stream))
+    return PreparedLaunch(lib.kvq_mse_unpack_decode, args, "kvq_mse_unpack_decode", (cb, packed1, norms, out))
 
 
 def kvq_rvq_unpack_decode(cb: Codebooks, packed1, packed2, norms, out, s_offset: int = 0, stream=None) -> None:
