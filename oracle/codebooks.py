@@ -11,8 +11,10 @@ What the pages fix (VeloxQuant-MLX blog):
     need no calibration data.
 
 Readings taken where the pages are silent:
-  * Stage 1 is the 2**b-level Lloyd-Max quantizer of N(0, sigma1**2) with sigma1**2 = 1/D,
-    the per-coordinate variance of a rotated unit vector.
+  * Stage 1 is the 2**b-level Lloyd-Max quantizer of N(0, sigma1**2) with sigma1**2 = 1/P,
+    the per-coordinate variance of a rotated unit vector of P coordinates. P = D for a
+    power-of-two head dimension; any other D (a multiple of 8) is rotated zero-padded to the
+    next power of two P (see rvq.py), so its tables are those of P.
   * Stage 2 is the 2**b-level Lloyd-Max quantizer of a zero-mean Laplace density whose
     variance equals the stage-1 mean squared error, sigma2**2 = MSE_G(b) * sigma1**2,
     where MSE_G(b) is the distortion of the unit-variance Gaussian Lloyd-Max quantizer.
@@ -114,7 +116,7 @@ def gaussian_mse(pos: np.ndarray) -> float:
 
 @dataclass(frozen=True)
 class Tables:
-    d: int
+    d: int  # head dimension: coordinates of an input and of a reconstruction
     bits: int
     sigma1: float
     sigma2: float
@@ -123,6 +125,7 @@ class Tables:
     b1: np.ndarray  # float32 [2**bits - 1]
     c2: np.ndarray
     b2: np.ndarray
+    p: int = 0  # rotation length: the power of two >= d (the number of codes per vector)
 
 
 def midpoints32(c32: np.ndarray) -> np.ndarray:
@@ -131,15 +134,25 @@ def midpoints32(c32: np.ndarray) -> np.ndarray:
     return (0.5 * (c[:-1] + c[1:])).astype(np.float32)
 
 
+def rotation_length(d: int) -> int:
+    """The power of two >= d: the length of the Hadamard rotation (d itself when d is one)."""
+    p = 1
+    while p < d:
+        p *= 2
+    return p
+
+
 def build_tables(d: int, bits: int) -> Tables:
-    """Both stages' float32 centroid and boundary tables for head dimension d."""
+    """Both stages' float32 centroid and boundary tables for head dimension d (rotated at
+    length P = rotation_length(d))."""
     if bits < 1 or bits > 4:
         raise ValueError("bits must be in 1..4")
     g = lloyd_max_positive_half(bits, "gauss")
     lap = lloyd_max_positive_half(bits, "laplace")
     mse = gaussian_mse(g)
-    sigma1 = 1.0 / math.sqrt(d)
+    P = rotation_length(d)
+    sigma1 = 1.0 / math.sqrt(P)
     sigma2 = math.sqrt(mse) * sigma1
     c1 = (sigma1 * full_codebook(g)).astype(np.float32)
     c2 = (sigma2 * full_codebook(lap)).astype(np.float32)
-    return Tables(d, bits, sigma1, sigma2, mse, c1, midpoints32(c1), c2, midpoints32(c2))
+    return Tables(d, bits, sigma1, sigma2, mse, c1, midpoints32(c1), c2, midpoints32(c2), P)

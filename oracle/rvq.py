@@ -2,7 +2,14 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Per head vector x (fp16, length D), following the VeloxQuant-MLX blog:
+Per head vector x (fp16, length D), following the VeloxQuant-MLX blog. A head dimension D
+that is not a power of two (a multiple of 8) is taken as the vector zero-padded to
+P = the next power of two: the norm is unchanged, the rotation below is of length P (the
+padded coordinates' signs are +1; they multiply zeros), all P rotated coordinates are
+quantized and packed, and the decode reconstructs P coordinates and returns the first D.
+(The pages' fused kernel takes only powers of two and leaves other shapes to a fallback:
+"rvq" tag page, "Wired in as a fallback, not a replacement"; zero-padding is this codec's
+reading of how such shapes are stored.) For a power of two, P = D and nothing changes.
   1. n = ||x||, u = x / n (u = 0 when n = 0).  ["rvq" tag page, "The pipeline, as it
      actually runs": the cache encodes the unit vector and keeps its norm; the norm is
      stored as float32.]
@@ -54,8 +61,19 @@ def _H(d: int) -> np.ndarray:
     return _H_CACHE[d]
 
 
-def norms_and_rotation(x16: np.ndarray, signs: np.ndarray):
-    """x16: float16 [N, D]; signs: +-1 [D].  Returns (norm float64 [N], y float32 [N, D]).
+def pad_to(x: np.ndarray, p: int, fill) -> np.ndarray:
+    """The last axis of x extended to length p with `fill`."""
+    d = x.shape[-1]
+    if d == p:
+        return x
+    out = np.full(x.shape[:-1] + (p,), fill, dtype=x.dtype)
+    out[..., :d] = x
+    return out
+
+
+def norms_and_rotation(x16: np.ndarray, signs: np.ndarray, p: int = 0):
+    """x16: float16 [N, D]; signs: +-1 [D]; p: rotation length (0: D).  Returns
+    (norm float64 [N], y float32 [N, P]): x and the signs are zero- and one-padded to P.
 
     The rotation is linear, so y = H diag(s) (x / n) / sqrt(D) = (H diag(s) x) / (n sqrt(D)).
     The oracle forms H diag(s) x on the float16 values themselves: every float16 is an
@@ -64,11 +82,12 @@ def norms_and_rotation(x16: np.ndarray, signs: np.ndarray):
     That product is therefore exact (exact cancellations give exactly 0), and the only
     roundings are the norm, the one division and the final rounding to float32.
     """
-    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    p = p or x16.shape[1]
+    x = pad_to(np.asarray(x16, dtype=np.float16).astype(np.float64), p, 0.0)
     n, d = x.shape
     if d > 1024:
         raise ValueError("exactness argument holds for D <= 1024")
-    s = np.asarray(signs, dtype=np.float64)
+    s = pad_to(np.asarray(signs, dtype=np.float64), p, 1.0)
     H = _H(d)
     norm = np.sqrt(np.sum(x * x, axis=1))
     y = np.empty((n, d), dtype=np.float32)
@@ -116,7 +135,7 @@ def encode(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
     x16 = np.asarray(x16, dtype=np.float16)
     if x16.ndim != 2 or x16.shape[1] != t.d:
         raise ValueError("x16 must be [N, D] with D matching the tables")
-    norm, y = norms_and_rotation(x16, signs)
+    norm, y = norms_and_rotation(x16, signs, t.p)
     i1 = np.empty(y.shape, dtype=np.uint8)
     i2 = np.empty(y.shape, dtype=np.uint8)
     r = np.empty(y.shape, dtype=np.float32)
@@ -135,11 +154,13 @@ def encode(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
 
 
 def _unrotate(z: np.ndarray, norms, signs: np.ndarray, d: int) -> np.ndarray:
-    """x_hat = RN16(n * diag(s) H z / sqrt(D)) (RN16(diag(s) H z / sqrt(D)) for norms=None),
-    products and sums in float64, rounded once."""
-    H = _H(d)
+    """x_hat = RN16(n * diag(s) H z / sqrt(P)) (RN16(diag(s) H z / sqrt(P)) for norms=None),
+    products and sums in float64, rounded once: z has P columns, x_hat the first d of the
+    P reconstructed coordinates."""
+    p = z.shape[1]
+    H = _H(p)
+    w = (z.astype(np.float64) @ H.T)[:, :d] / math.sqrt(p)
     s = np.asarray(signs, dtype=np.float64)
-    w = (z.astype(np.float64) @ H.T) / math.sqrt(d)
     u_hat = w * s[None, :]
     if norms is not None:
         u_hat = u_hat * np.asarray(norms, dtype=np.float32).astype(np.float64)[:, None]
@@ -148,11 +169,10 @@ def _unrotate(z: np.ndarray, norms, signs: np.ndarray, d: int) -> np.ndarray:
 
 def decode(packed1: np.ndarray, packed2: np.ndarray, norms, signs: np.ndarray, t: Tables) -> np.ndarray:
     """Decode [N, n_words] streams to float16 [N, D]; norms=None gives unit reconstructions."""
-    d = t.d
-    i1 = packing.unpack(packed1, t.bits, d)
-    i2 = packing.unpack(packed2, t.bits, d)
+    i1 = packing.unpack(packed1, t.bits, t.p)
+    i2 = packing.unpack(packed2, t.bits, t.p)
     z = (t.c1[i1] + t.c2[i2]).astype(np.float32)
-    return _unrotate(z, norms, signs, d)
+    return _unrotate(z, norms, signs, t.d)
 
 
 def encode_mse(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
@@ -163,7 +183,7 @@ def encode_mse(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
     x16 = np.asarray(x16, dtype=np.float16)
     if x16.ndim != 2 or x16.shape[1] != t.d:
         raise ValueError("x16 must be [N, D] with D matching the tables")
-    norm, y = norms_and_rotation(x16, signs)
+    norm, y = norms_and_rotation(x16, signs, t.p)
     i1 = np.empty(y.shape, dtype=np.uint8)
     for a in range(0, y.shape[0], CHUNK):
         i1[a:a + CHUNK] = nearest(y[a:a + CHUNK], t.c1)
@@ -173,5 +193,5 @@ def encode_mse(x16: np.ndarray, signs: np.ndarray, t: Tables) -> dict:
 def decode_mse(packed: np.ndarray, norms, signs: np.ndarray, t: Tables) -> np.ndarray:
     """Single-stage decode: z = c1[i] ("turboquant" tag page, "Kernel 2": dequantize is a
     gather of the centroid), then the inverse rotation and the norm."""
-    i1 = packing.unpack(packed, t.bits, t.d)
+    i1 = packing.unpack(packed, t.bits, t.p)
     return _unrotate(t.c1[i1].astype(np.float32), norms, signs, t.d)

@@ -224,7 +224,7 @@ def test_reconstruction_quality_band(bits):
 
 # ------------------------------------------------------------------------------ planted mistakes
 
-def _sign_after_h(x16, signs):
+def _sign_after_h(x16, signs, p=0):
     x = np.asarray(x16, np.float16).astype(np.float64)
     d = x.shape[1]
     n = np.sqrt(np.sum(x * x, axis=1))
@@ -286,6 +286,6 @@ def test_planted_packing_and_scale_mistakes_are_caught(monkeypatch):
         t = real(d, bits)
         lap = cb.full_codebook(cb.lloyd_max_positive_half(bits, "laplace"))
         c2 = (t.sigma1 * lap).astype(np.float32)
-        return cb.Tables(t.d, t.bits, t.sigma1, t.sigma1, t.mse_g, t.c1, t.b1, c2, cb.midpoints32(c2))
+        return cb.Tables(t.d, t.bits, t.sigma1, t.sigma1, t.mse_g, t.c1, t.b1, c2, cb.midpoints32(c2), t.p)
     monkeypatch.setattr(cb, "build_tables", same_scale)
     assert not _all_examples_pass()
