@@ -5,6 +5,8 @@ Inputs come from the seeded generator (synth) or are built by hand; the oracle a
 consumes the very bytes the device consumed, copied back to the host. Decoders are fed
 the oracle's packed words (uploaded), never words produced by the device.
 """
+import math
+
 import numpy as np
 import torch
 
@@ -21,11 +23,37 @@ REL_WINDOW = 1e-5
 MAX_FLIP_FRACTION = 1e-6
 
 
+# Tail probability a small sample's flip count may reach under the allowance below.
+SMALL_SAMPLE_TAIL = 1e-3
+
+
+def small_sample_allowance(n_codes: int) -> int:
+    """Flips a sample smaller than a workload may carry: the smallest k >= 1 that a Poisson
+    count with the cap's mean (1e-6 n) exceeds with probability at most 10^-3."""
+    lam = MAX_FLIP_FRACTION * n_codes
+    k, term = 0, math.exp(-lam)
+    cdf = term
+    while k < 1 or 1.0 - cdf > SMALL_SAMPLE_TAIL:
+        k += 1
+        term *= lam / k
+        cdf += term
+    return k
+
+
+# Codes of the smallest workload: samples of at least this many are held to the rate itself.
+WORKLOAD_CODES = 10 ** 7
+
+
 def flip_cap(n_codes: int) -> float:
-    """The 1e-6 cap is a rate over a workload (every workload has > 10^7 codes). A sample
-    of fewer than 10^6 codes would be held to zero flips by the literal fraction, so such
-    samples may carry one in-window, one-level flip; larger ones get the rate itself."""
-    return max(MAX_FLIP_FRACTION, 1.0 / max(1, n_codes))
+    """The 1e-6 cap is a rate over a workload (every workload has more than 10^7 codes),
+    which a smaller sample cannot resolve: at the cap's rate a sample of 10^5 codes holds
+    0.1 flips on average, and two now and then. A smaller sample is therefore held to the
+    count that the cap's rate exceeds with probability 10^-3 (each flip still in-window and
+    one level), and every sample of a session is pooled and the pool held to the rate
+    itself (tests/test_zy_pooled_flips.py); workload-sized samples get the rate itself."""
+    if n_codes >= WORKLOAD_CODES:
+        return MAX_FLIP_FRACTION
+    return max(MAX_FLIP_FRACTION, small_sample_allowance(n_codes) / max(1, n_codes))
 
 
 # Every sample judged under flip_cap in this session, pooled: one allowed flip per small

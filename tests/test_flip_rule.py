@@ -98,3 +98,19 @@ def test_padding_and_norm_are_checked():
     norms[2] *= np.float32(1.0 + 1e-4)
     rep = flips.compare_encode(ref["packed1"], ref["packed2"], norms, ref, t, REL)
     assert 5e-5 < rep.norm_max_rel < 2e-4 and not rep.ok(1.0, 1e-6)
+
+
+def test_small_sample_allowance_is_the_poisson_tail_bound():
+    """The per-sample flip allowance of the GPU parity tests: the smallest k >= 1 with
+    P(Poisson(1e-6 n) > k) <= 1e-3, checked against scipy's Poisson survival function."""
+    from scipy import stats
+
+    from tests import gpu_util as gu
+    for n in [1, 10, 1000, 10 ** 5, 384_000, 768_256, 10 ** 6, 3 * 10 ** 6, 10 ** 7 - 1]:
+        k = gu.small_sample_allowance(n)
+        lam = gu.MAX_FLIP_FRACTION * n
+        assert k >= 1 and stats.poisson.sf(k, lam) <= gu.SMALL_SAMPLE_TAIL
+        assert k == 1 or stats.poisson.sf(k - 1, lam) > gu.SMALL_SAMPLE_TAIL
+        assert gu.flip_cap(n) * n >= k
+    for n in [10 ** 7, 10 ** 9]:  # workload-sized samples: the rate itself
+        assert gu.flip_cap(n) == gu.MAX_FLIP_FRACTION

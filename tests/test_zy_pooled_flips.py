@@ -1,6 +1,7 @@
-"""The small-sample allowance, pooled. Samples of fewer than 10^6 codes may each carry one
-in-window flip (tests/gpu_util.py, flip_cap); over every such sample judged in this
-session together, the flips must still stay within the 1e-6 rate of all their codes. Runs
+"""The small-sample allowance, pooled. Samples smaller than a workload may each carry the
+few in-window flips that a Poisson count at the 1e-6 rate reaches with probability 10^-3
+(tests/gpu_util.py, flip_cap); over every sample judged in this session together, the
+flips must still stay within the 1e-6 rate of all their codes. Runs
 after the other GPU tests (pytest collects files in name order); alone, it has nothing to
 judge and skips."""
 import pytest
