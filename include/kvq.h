@@ -32,7 +32,7 @@ extern "C" {
 typedef enum kvq_status {
   KVQ_OK = 0,
   KVQ_ERR_ARG = -1,    /* a required pointer is NULL, or a codebook struct is inconsistent */
-  KVQ_ERR_SHAPE = -2,  /* d not a power of two in [8, 1024]; bits not in 1..4; B, H, S < 0 */
+  KVQ_ERR_SHAPE = -2,  /* d not a multiple of 8 in [8, 1024] (a power of two where stated); bits not in 1..4; B, H, S < 0 */
   KVQ_ERR_ALIGN = -3,  /* an fp16 or packed-word buffer not 16-byte aligned, or a norm buffer not 4-byte aligned */
   KVQ_ERR_RANGE = -4,  /* s_offset < 0, s_offset + S > S_cap, or a size overflows 64 bits */
   KVQ_ERR_DEVICE = -5  /* the HIP launch reported an error */
@@ -46,26 +46,32 @@ typedef enum kvq_status {
  * Codebooks and rotation signs for one (d, bits) pair. Plain data, 416 bytes; build it
  * with kvq_build_codebooks and treat it as read-only.
  *
+ * The rotation length P is d rounded up to a power of two (P = d when d is one). The
+ * Walsh-Hadamard transform exists at powers of two only, so a head dimension such as 96 or
+ * 576 is rotated as the vector padded with P - d zeros, and all P rotated coordinates are
+ * coded (the zeros add nothing to the norm, and the rotated vector keeps unit norm).
+ *
  * c1/b1: stage-1 centroids (2^bits, ascending) and boundaries (2^bits - 1): the
- *        Lloyd-Max quantizer of N(0, sigma1^2), sigma1^2 = 1/d (the variance of one
+ *        Lloyd-Max quantizer of N(0, sigma1^2), sigma1^2 = 1/P (the variance of one
  *        coordinate of a rotated unit vector).
  * c2/b2: stage-2 tables: the Lloyd-Max quantizer of a zero-mean Laplace density whose
  *        variance is the stage-1 distortion, sigma2^2 = mse_g * sigma1^2.
  *        Boundaries are the float32-rounded midpoints of neighbouring centroids (blog,
  *        "rvq" tag page, "What 'quantize' means here, precisely"); both tables are exactly
  *        antisymmetric, so the middle boundary is +0.0.
- * sign_bits: bit j (word j/32, bit j%32) set <=> the rotation multiplies coordinate j by -1.
+ * sign_bits: bit j (word j/32, bit j%32) set <=> the rotation multiplies coordinate j by -1
+ *        (j < d; the padding coordinates take +1 and their bits are ignored).
  */
 typedef struct kvq_codebooks {
   int32_t d;               /* head dimension */
   int32_t bits;            /* bits per code, per stage */
   int32_t elems_per_word;  /* floor(32 / bits) codes in each uint32 word */
-  int32_t n_words;         /* ceil(d / elems_per_word) words per vector per stream */
+  int32_t n_words;         /* ceil(P / elems_per_word) words per vector per stream */
   float c1[16];
   float b1[15];
   float c2[16];
   float b2[15];
-  double sigma1;           /* 1/sqrt(d) */
+  double sigma1;           /* 1/sqrt(P) */
   double sigma2;           /* sqrt(mse_g) * sigma1 */
   double mse_g;            /* distortion of the unit-variance Gaussian Lloyd-Max quantizer */
   uint32_t sign_bits[KVQ_MAX_D / 32];
@@ -73,7 +79,7 @@ typedef struct kvq_codebooks {
 
 /*
  * kvq_build_codebooks - host only, no device calls.
- *   d     head dimension, a power of two in [8, 1024]
+ *   d     head dimension, a multiple of 8 in [8, 1024]
  *   bits  bits per code per stage, 1..4
  *   signs host array of d entries, each +1 or -1 (the rotation's sign vector), or NULL
  *         for all +1
@@ -99,12 +105,12 @@ kvq_status kvq_build_codebooks(int32_t d, int32_t bits, const int8_t* signs, kvq
  *   s_offset  token s of x is written at cache position s_offset + s (appending one
  *             decode step at a time is S = 1, s_offset = step)
  *   stream    hipStream_t or NULL
- * Word layout (blog, "rvq" tag page, "The kernel"): code j of a vector goes to word
+ * Word layout (blog, "rvq" tag page, "The kernel"): code j of a vector (j < P) goes to word
  * j / elems_per_word at bits [(j % elems_per_word) * bits, ... + bits), LSB first; bits
  * past the last code are 0. Code value = the number of boundaries the value exceeds
  * ("What 'quantize' means here, precisely"), stage 1 on the rotated coordinate
- * y = (H diag(s) x)_j / (sqrt(d) ||x||), stage 2 on the float32 residual y - c1[code1].
- * A zero vector stores norm 0 and the codes of y = 0.
+ * y = (H diag(s) x)_j / (sqrt(P) ||x||) of x padded with zeros to length P, stage 2 on the
+ * float32 residual y - c1[code1]. A zero vector stores norm 0 and the codes of y = 0.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_SHAPE, KVQ_ERR_ALIGN, KVQ_ERR_RANGE (checked before any
  * HIP call), KVQ_ERR_DEVICE (launch error). The packed outputs and x must not overlap.
  */
@@ -120,8 +126,9 @@ kvq_status kvq_rvq_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
  *   norms            device float32 [B, H, S_cap], or NULL for unit-norm reconstructions
  *   x_out            device fp16 [B, H, S, d], contiguous, 16-byte aligned
  * Each coordinate is dequantized as c1[i1] + c2[i2] in the rotated domain (blog,
- * "turboquant" tag page, "Kernel 5"), rotated back by diag(s) H / sqrt(d) (H is
- * symmetric and H H = d I), scaled by the norm and rounded to fp16 (nearest-even).
+ * "turboquant" tag page, "Kernel 5"), rotated back by diag(s) H / sqrt(P) (H is
+ * symmetric and H H = P I), scaled by the norm and rounded to fp16 (nearest-even); the
+ * first d of the P coordinates are written.
  * Errors as for kvq_rvq_encode_pack.
  */
 kvq_status kvq_rvq_unpack_decode(const kvq_codebooks* cb,
@@ -149,7 +156,7 @@ kvq_status kvq_mse_encode_pack(const kvq_codebooks* cb, const uint16_t* x,
 /*
  * kvq_mse_unpack_decode - device. Inverse of kvq_mse_encode_pack: each coordinate is
  * dequantized as c1[i] (blog, "turboquant" tag page, "Kernel 2", dequantize: a gather of
- * the centroid), rotated back by diag(s) H / sqrt(d), scaled by the norm (or not, for
+ * the centroid), rotated back by diag(s) H / sqrt(P), scaled by the norm (or not, for
  * norms = NULL) and rounded to fp16 (nearest-even). Arguments and errors as for
  * kvq_rvq_unpack_decode with the single code stream `packed`.
  */
@@ -166,7 +173,7 @@ kvq_status kvq_mse_unpack_decode(const kvq_codebooks* cb, const uint32_t* packed
  * every bit set. Bits are packed LSB-first, 32 per word: bit j at word j / 32, bit j % 32;
  * bits past d are 0.
  *   cb        from kvq_build_codebooks(d, 1, signs): only d and the signs are used;
- *             bits != 1 is KVQ_ERR_SHAPE
+ *             bits != 1 or a d that is not a power of two is KVQ_ERR_SHAPE
  *   packed    device uint32 [B, H, S_cap, ceil(d / 32)], 16-byte aligned
  *   norms     device float32 [B, H, S_cap]: ||x|| (the magnitude)
  *   other arguments and errors as for kvq_rvq_encode_pack
@@ -218,8 +225,8 @@ kvq_status kvq_qjl_encode_pack(const uint16_t* sketch, int32_t d, int32_t m, con
  * kvq_rvq_unpack_decode would round to fp16 (no rounding is applied to them here). Every
  * query attends to all S_kv cached positions (no mask). The work runs in the rotated
  * domain: q . khat_t = n_t (R q) . z_t, and the weighted sum of values is rotated back once.
- *   cbk, cbv     codebooks of the key and of the value cache (same d and bits; the sign
- *                vectors may differ)
+ *   cbk, cbv     codebooks of the key and of the value cache (same d and bits, d a power
+ *                of two; the sign vectors may differ)
  *   q            device fp16 [B, Hq, Sq, d], contiguous, 16-byte aligned
  *   Hkv          key/value heads; Hq must be a multiple of Hkv (query head h reads
  *                key/value head h / (Hq / Hkv))
@@ -232,7 +239,7 @@ kvq_status kvq_qjl_encode_pack(const uint16_t* sketch, int32_t d, int32_t m, con
  *                aligned, owned by the caller; its contents are overwritten
  *   out          device fp16 [B, Hq, Sq, d], contiguous, 16-byte aligned
  * Errors: KVQ_ERR_ARG (null pointer, non-finite scale, inconsistent codebooks),
- * KVQ_ERR_SHAPE (codebooks of different d or bits, negative sizes, Hq not a multiple of
+ * KVQ_ERR_SHAPE (codebooks of different d or bits, d not a power of two, negative sizes, Hq not a multiple of
  * Hkv), KVQ_ERR_ALIGN, KVQ_ERR_RANGE (S_kv out of range, workspace too small, overflow),
  * KVQ_ERR_DEVICE. B * Hq * Sq == 0 returns KVQ_OK without touching any pointer.
  */

@@ -129,9 +129,19 @@ def _check(status: int, what: str) -> None:
         raise KvqError(status, what)
 
 
+def rotation_length(d: int) -> int:
+    """The power of two (at least 8) that head dimension d is rotated at: a d that is not a
+    power of two is zero-padded to it, and all of its rotated coordinates are coded."""
+    p = 8
+    while p < d:
+        p *= 2
+    return p
+
+
 def n_words(d: int, bits: int) -> int:
+    """Packed words per vector per stream for head dimension d."""
     epw = 32 // bits
-    return (d + epw - 1) // epw
+    return (rotation_length(d) + epw - 1) // epw
 
 
 def kvq_build_codebooks(d: int, bits: int, signs=None) -> Codebooks:

@@ -63,10 +63,10 @@ bool stage_tables_ok(const float* c, const float* b, int bits) {
 
 kvq_status check_codebooks(const kvq_codebooks* cb) {
   if (cb == nullptr) return KVQ_ERR_ARG;
-  if (cb->d < KVQ_MIN_D || cb->d > KVQ_MAX_D || !is_pow2(cb->d)) return KVQ_ERR_SHAPE;
+  if (cb->d < KVQ_MIN_D || cb->d > KVQ_MAX_D || cb->d % 8 != 0) return KVQ_ERR_SHAPE;
   if (cb->bits < 1 || cb->bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
-  const int epw = 32 / cb->bits;
-  if (cb->elems_per_word != epw || cb->n_words != (cb->d + epw - 1) / epw) return KVQ_ERR_ARG;
+  const int epw = 32 / cb->bits, p = kvq::rotation_length(cb->d);
+  if (cb->elems_per_word != epw || cb->n_words != (p + epw - 1) / epw) return KVQ_ERR_ARG;
   if (!stage_tables_ok(cb->c1, cb->b1, cb->bits) || !stage_tables_ok(cb->c2, cb->b2, cb->bits)) return KVQ_ERR_ARG;
   return KVQ_OK;
 }
@@ -77,7 +77,10 @@ kvq_status check_tiles(int64_t n_vec, int64_t vectors_per_tile) {
                                                                                                  : KVQ_OK;
 }
 
-int sign_of(const kvq_codebooks* cb, int j) { return ((cb->sign_bits[j >> 5] >> (j & 31)) & 1u) ? -1 : 1; }
+// Sign of rotated coordinate j; the padding coordinates (j >= d) take +1.
+int sign_of(const kvq_codebooks* cb, int j) {
+  return j < cb->d && ((cb->sign_bits[j >> 5] >> (j & 31)) & 1u) ? -1 : 1;
+}
 
 // Validates the shared shape/range arguments; on success returns the vector count.
 kvq_status check_sizes(const kvq_codebooks* cb, int64_t B, int64_t H, int64_t S, int64_t S_cap,
@@ -160,8 +163,9 @@ float as_float(int32_t v) {
 }
 
 kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
-  const int d = cb->d, bits = cb->bits;
+  const int d = kvq::rotation_length(cb->d), bits = cb->bits;  // the rotation's length
   const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
+  a->dch = cb->d / 8;
   std::memset(a->wpair, 0, sizeof(a->wpair));
   std::memset(a->tab1, 0, sizeof(a->tab1));
   std::memset(a->tab2, 0, sizeof(a->tab2));
@@ -204,8 +208,9 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
 
 // stages = 2: entry (i1 << bits) | i2 is c1[i1] + c2[i2]; stages = 1: entry i1 << bits is c1[i1].
 void fill_decode_args(const kvq_codebooks* cb, int stages, DecodeArgs* a) {
-  const int d = cb->d, bits = cb->bits, k = 1 << bits;
+  const int d = kvq::rotation_length(cb->d), bits = cb->bits, k = 1 << bits;  // the rotation's length
   a->inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  a->dch = cb->d / 8;
   std::memset(a->ztab, 0, sizeof(a->ztab));
   for (int i1 = 0; i1 < k; ++i1) {
     if (stages == 1) {
@@ -224,7 +229,7 @@ kvq_status encode_pack(const kvq_codebooks* cb, int stages, const uint16_t* x, i
                        void* stream) {
   kvq_status st = check_codebooks(cb);
   if (st != KVQ_OK) return st;
-  if (stages == 0 && cb->bits != 1) return KVQ_ERR_SHAPE;
+  if (stages == 0 && (cb->bits != 1 || !is_pow2(cb->d))) return KVQ_ERR_SHAPE;
   int64_t n_vec = 0;
   st = check_sizes(cb, B, H, S, S_cap, s_offset, &n_vec);
   if (st != KVQ_OK) return st;

@@ -90,7 +90,7 @@ void fill_tables(int bits, const double* pos, double sigma, float* c, float* b) 
 
 extern "C" kvq_status kvq_build_codebooks(int32_t d, int32_t bits, const int8_t* signs, kvq_codebooks* out) {
   if (out == nullptr) return KVQ_ERR_ARG;
-  if (d < KVQ_MIN_D || d > KVQ_MAX_D || (d & (d - 1)) != 0) return KVQ_ERR_SHAPE;
+  if (d < KVQ_MIN_D || d > KVQ_MAX_D || d % 8 != 0) return KVQ_ERR_SHAPE;
   if (bits < 1 || bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
   if (signs != nullptr)
     for (int j = 0; j < d; ++j)
@@ -101,13 +101,17 @@ extern "C" kvq_status kvq_build_codebooks(int32_t d, int32_t bits, const int8_t*
   cb.d = d;
   cb.bits = bits;
   cb.elems_per_word = 32 / bits;
-  cb.n_words = (d + cb.elems_per_word - 1) / cb.elems_per_word;
+  // Any other head dimension is rotated zero-padded to the next power of two P (its codes
+  // are those of all P rotated coordinates), so the tables are those of P.
+  int p = 8;
+  while (p < d) p *= 2;
+  cb.n_words = (p + cb.elems_per_word - 1) / cb.elems_per_word;
 
   double g[8], l[8];
   lloyd_max_half(bits, false, g);
   lloyd_max_half(bits, true, l);
   cb.mse_g = gauss_distortion(bits, g);
-  cb.sigma1 = 1.0 / std::sqrt(static_cast<double>(d));
+  cb.sigma1 = 1.0 / std::sqrt(static_cast<double>(p));
   cb.sigma2 = std::sqrt(cb.mse_g) * cb.sigma1;
   fill_tables(bits, g, cb.sigma1, cb.c1, cb.b1);
   fill_tables(bits, l, cb.sigma2, cb.c2, cb.b2);
@@ -122,7 +126,7 @@ extern "C" const char* kvq_status_str(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_ARG: return "invalid argument (null pointer or inconsistent codebooks)";
-    case KVQ_ERR_SHAPE: return "unsupported shape (d must be a power of two in [8,1024], bits in 1..4, sizes >= 0)";
+    case KVQ_ERR_SHAPE: return "unsupported shape (d must be a multiple of 8 in [8,1024], bits in 1..4, sizes >= 0)";
     case KVQ_ERR_ALIGN: return "misaligned buffer (fp16 and packed-word buffers need 16-byte, norm buffers 4-byte alignment)";
     case KVQ_ERR_RANGE: return "out of range (s_offset + S exceeds S_cap, or a size overflows)";
     case KVQ_ERR_DEVICE: return "HIP launch failed";

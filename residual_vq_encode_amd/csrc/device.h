@@ -246,6 +246,23 @@ __device__ __forceinline__ void dma_tile(uint4* buf, const uint4* src, int nrows
   }
 }
 
+// Direct-to-LDS loads of a tile of padded rows: the tile's nchunks real 16-byte chunks
+// (rows of dch chunks, contiguous in HBM from src) land densely in LDS slots [0, nchunks);
+// instruction k writes slots [64k, 64k + 64), and lanes past nchunks re-read the tile's last
+// chunk, so every load stays inside the input. NI instructions cover up to 64 NI chunks.
+template <int NI>
+__device__ __forceinline__ void dma_dense(uint4* buf, const uint4* src, int nchunks, int lane) {
+  const char* base = reinterpret_cast<const char*>(src);  // wave-uniform
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    if (64 * k < nchunks) {  // wave-uniform
+      const int s = k * 64 + lane;
+      const uint32_t off = static_cast<uint32_t>(s < nchunks ? s : nchunks - 1) * 16u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf + k * 64), 16, 0, kNonTemporal);
+    }
+  }
+}
+
 // Cache row of flattened input vector v0 + i: (v / S) * S_cap + s_offset + v % S.
 // CONTIG (S == S_cap, s_offset == 0, chosen on the host) compiles to v0 + i. i < 64.
 template <bool CONTIG>

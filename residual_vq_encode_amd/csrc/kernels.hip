@@ -135,7 +135,10 @@ __device__ __forceinline__ void quantize_run(const float (&y)[N], float K, float
 // centroid), stream 1 only; STAGES = 0 (BITS = 1 only): the 1-bit sign code [y >= 0] of
 // the rotated vector with its norm ("rvq" tag page, "A fusion this codebase had already
 // proven out": rotate, binarize, pack and magnitude in one kernel), stream 1 only.
-template <int D, int BITS, bool CONTIG, int STAGES>
+// D is the rotation length. PAD: the input rows hold a.dch < D / 8 chunks (a head
+// dimension that is not a power of two); the rows are loaded densely and the missing
+// chunks read as zeros, which is the zero-padded vector the codec rotates.
+template <int D, int BITS, bool CONTIG, int STAGES, bool PAD = false>
 __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>())) void encode_kernel(const EncodeArgs a) {
   using G = Layout<D>;
   constexpr int C = G::C, L = G::L, LOG_L = G::LOG_L, VW = G::VW, CH = G::CH;
@@ -196,11 +199,21 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
 #pragma unroll
   for (int p = 0; p < C / 2; ++p) wt[p] = a.wpair[q * (C / 2) + p];
 
+  // PAD: tile t's rows start at chunk t VW dch, and this lane's chunk c of its slice is
+  // chunk C q / 8 + c of its vector, real when below dch
+  const int dch = PAD ? a.dch : D / 8;
+  auto load_tile = [&](int t, int nvt) {
+    if constexpr (PAD) {
+      dma_dense<CH>(buf, x16 + static_cast<int64_t>(t) * VW * dch, nvt * dch, lane);
+    } else {
+      dma_tile<CH>(buf, x16 + static_cast<int64_t>(t) * 64 * CH, nvt * L, lane);
+    }
+  };
   int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
   if (tile < n_tiles) {
     const int64_t v0 = static_cast<int64_t>(tile) * VW;
     const int nv = static_cast<int>(a.n_vec - v0 < VW ? a.n_vec - v0 : VW);
-    dma_tile<CH>(buf, x16 + static_cast<int64_t>(tile) * 64 * CH, nv * L, lane);
+    load_tile(tile, nv);
   }
   // The previous tile's results wait in registers until the current tile has been read out
   // of LDS: storing them right after they are computed would put the stores between the
@@ -278,7 +291,13 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
     float y[C];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const uint4 v = buf[rbase ^ c];
+      uint4 v;
+      if constexpr (PAD) {
+        const int cv = q * CH + c;
+        v = cv < dch ? buf[vl * dch + cv] : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        v = buf[rbase ^ c];
+      }
       const uint32_t xh[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -302,7 +321,7 @@ __global__ __launch_bounds__(kBlockThreads, (encode_waves_per_eu<BITS, CONTIG>()
       if (nt < n_tiles) {
         const int64_t w0 = static_cast<int64_t>(nt) * VW;
         const int nvn = static_cast<int>(a.n_vec - w0 < VW ? a.n_vec - w0 : VW);
-        dma_tile<CH>(buf, x16 + static_cast<int64_t>(nt) * 64 * CH, nvn * L, lane);
+        load_tile(nt, nvn);
       }
     }
 
@@ -668,8 +687,10 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
 // ------------------------------------------------------------------------------ decode
 
 // STAGES = 2: z = c1[i1] + c2[i2]; STAGES = 1: z = c1[i1] (the host fills the table so that
-// entry (i1 << BITS) holds the right value in both cases).
-template <int D, int BITS, bool CONTIG, int STAGES>
+// entry (i1 << BITS) holds the right value in both cases). D is the rotation length. PAD:
+// the output rows hold a.dch < D / 8 chunks (a head dimension that is not a power of two):
+// of the D reconstructed coordinates, the first 8 dch are stored.
+template <int D, int BITS, bool CONTIG, int STAGES, bool PAD = false>
 __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kernel(const DecodeArgs a) {
   using G = Layout<D>;
   using S = CodeShape<D, BITS>;
@@ -742,11 +763,20 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
   };
   u32x4_t out[CH];          // previous tile's output chunks (chunk 64k + lane of that tile)
   int out_tile = -1, out_rows = 0;
+  const int dch = PAD ? a.dch : D / 8;  // chunks of an output row
   auto flush = [&]() {
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x) + static_cast<int64_t>(out_tile) * 64 * CH;
+    if constexpr (PAD) {
+      // chunk s of the tile's dense output (rows of dch chunks; out_rows is its chunk count)
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x) + static_cast<int64_t>(out_tile) * VW * dch;
 #pragma unroll
-    for (int k = 0; k < CH; ++k)
-      if ((k * 64 + lane) / CH < out_rows) __builtin_nontemporal_store(out[k], dst + k * 64 + lane);
+      for (int k = 0; k < CH; ++k)
+        if (k * 64 + lane < out_rows) __builtin_nontemporal_store(out[k], dst + k * 64 + lane);
+    } else {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.x) + static_cast<int64_t>(out_tile) * 64 * CH;
+#pragma unroll
+      for (int k = 0; k < CH; ++k)
+        if ((k * 64 + lane) / CH < out_rows) __builtin_nontemporal_store(out[k], dst + k * 64 + lane);
+    }
   };
 
   int tile = static_cast<int>(blockIdx.x) * kWavesPerBlock + wv;
@@ -784,15 +814,27 @@ __global__ __launch_bounds__(kBlockThreads, kDecodeWavesPerEU) void decode_kerne
           make_uint4(o[4 * c] ^ mk.x, o[4 * c + 1] ^ mk.y, o[4 * c + 2] ^ mk.z, o[4 * c + 3] ^ mk.w);
     }
     wave_lds_fence();
+    if constexpr (PAD) {
+      // dense output chunk s = 64k + lane is chunk cv = s % dch of vector s / dch, which row
+      // (s / dch) L + cv / CH of the tile holds as its chunk cv % CH
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int g = k * 64 + lane, r = g / CH, c = g % CH;
-      const uint4 v = buf[r * CH + (c ^ swz<CH>(r))];
-      out[k] = u32x4_t{v.x, v.y, v.z, v.w};
+      for (int k = 0; k < CH; ++k) {
+        const int sidx = k * 64 + lane, vv = sidx / dch, cv = sidx - vv * dch;
+        const int r = vv * L + cv / CH, c = cv % CH;
+        const uint4 v = r < 64 ? buf[r * CH + (c ^ swz<CH>(r))] : make_uint4(0u, 0u, 0u, 0u);
+        out[k] = u32x4_t{v.x, v.y, v.z, v.w};
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const int g = k * 64 + lane, r = g / CH, c = g % CH;
+        const uint4 v = buf[r * CH + (c ^ swz<CH>(r))];
+        out[k] = u32x4_t{v.x, v.y, v.z, v.w};
+      }
     }
     wave_lds_fence();
     out_tile = tile;
-    out_rows = nv * L;
+    out_rows = PAD ? nv * dch : nv * L;
   }
   if (out_tile >= 0) flush();
 }
@@ -847,78 +889,92 @@ static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* 
   return hipLaunchKernel(f, dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), a, 0, stream);
 }
 
-template <int D, int BITS, int STAGES>
+template <int D, int BITS, int STAGES, bool PAD>
 static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   static int cap[2][2] = {{0, 0}, {0, 0}};
   const bool c = a.map.contiguous != 0;
-  if constexpr (encode_on_matrix_cores(D, BITS)) {
+  if constexpr (encode_on_matrix_cores(D, BITS) && !PAD) {
     const void* f = c ? reinterpret_cast<const void*>(&encode_mx_kernel<BITS, true, STAGES>)
                       : reinterpret_cast<const void*>(&encode_mx_kernel<BITS, false, STAGES>);
     return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, kMxTile, cap[c ? 1 : 0], true, stream);
   } else {
-    const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES>)
-                      : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES>);
+    const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES, PAD>)
+                      : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES, PAD>);
     return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
   }
 }
 
-template <int D, int BITS, int STAGES>
+template <int D, int BITS, int STAGES, bool PAD>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   static int cap[2][2] = {{0, 0}, {0, 0}};
   const bool c = a.map.contiguous != 0;
-  const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES>)
-                    : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES>);
+  const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES, PAD>)
+                    : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES, PAD>);
   return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
 }
 
-#define KVQ_FOR_BITS(MACRO, D, S) \
-  case 1: return MACRO<D, 1, S>; case 2: return MACRO<D, 2, S>; case 3: return MACRO<D, 3, S>; case 4: return MACRO<D, 4, S>;
+#define KVQ_FOR_BITS(MACRO, D, S, P)                                                        \
+  case 1: return MACRO<D, 1, S, P>; case 2: return MACRO<D, 2, S, P>; case 3: return MACRO<D, 3, S, P>; \
+  case 4: return MACRO<D, 4, S, P>;
 
-template <int D>
+// PAD: the head dimension is below the rotation length D (a multiple of 8 that is not a power
+// of two, so at least 24 and D at least 32); the sign code takes powers of two only.
+template <int D, bool PAD>
 static auto encode_fn(int bits, int stages) -> hipError_t (*)(const EncodeArgs&, hipStream_t) {
-  if (stages == 2) {
-    switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 2) }
-  } else if (stages == 1) {
-    switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 1) }
-  } else if (stages == 0 && bits == 1) {
-    return launch_encode_t<D, 1, 0>;
+  if constexpr (PAD && D < 32) {
+    return nullptr;
+  } else {
+    if (stages == 2) {
+      switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 2, PAD) }
+    } else if (stages == 1) {
+      switch (bits) { KVQ_FOR_BITS(launch_encode_t, D, 1, PAD) }
+    } else if (stages == 0 && bits == 1 && !PAD) {
+      return launch_encode_t<D, 1, 0, false>;
+    }
+    return nullptr;
   }
-  return nullptr;
 }
-template <int D>
+template <int D, bool PAD>
 static auto decode_fn(int bits, int stages) -> hipError_t (*)(const DecodeArgs&, hipStream_t) {
-  if (stages == 2) {
-    switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 2) }
-  } else if (stages == 1) {
-    switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 1) }
+  if constexpr (PAD && D < 32) {
+    return nullptr;
+  } else {
+    if (stages == 2) {
+      switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 2, PAD) }
+    } else if (stages == 1) {
+      switch (bits) { KVQ_FOR_BITS(launch_decode_t, D, 1, PAD) }
+    }
+    return nullptr;
   }
-  return nullptr;
 }
 
-#define KVQ_FOR_D(FN, bits, stages)               \
-  switch (d) {                                    \
-    case 8: f = FN<8>(bits, stages); break;       \
-    case 16: f = FN<16>(bits, stages); break;     \
-    case 32: f = FN<32>(bits, stages); break;     \
-    case 64: f = FN<64>(bits, stages); break;     \
-    case 128: f = FN<128>(bits, stages); break;   \
-    case 256: f = FN<256>(bits, stages); break;   \
-    case 512: f = FN<512>(bits, stages); break;   \
-    case 1024: f = FN<1024>(bits, stages); break; \
-    default: break;                               \
+#define KVQ_FOR_D(FN, bits, stages, pad)                                              \
+  switch (p) {                                                                        \
+    case 8: f = pad ? FN<8, true>(bits, stages) : FN<8, false>(bits, stages); break;  \
+    case 16: f = pad ? FN<16, true>(bits, stages) : FN<16, false>(bits, stages); break; \
+    case 32: f = pad ? FN<32, true>(bits, stages) : FN<32, false>(bits, stages); break; \
+    case 64: f = pad ? FN<64, true>(bits, stages) : FN<64, false>(bits, stages); break; \
+    case 128: f = pad ? FN<128, true>(bits, stages) : FN<128, false>(bits, stages); break; \
+    case 256: f = pad ? FN<256, true>(bits, stages) : FN<256, false>(bits, stages); break; \
+    case 512: f = pad ? FN<512, true>(bits, stages) : FN<512, false>(bits, stages); break; \
+    case 1024: f = pad ? FN<1024, true>(bits, stages) : FN<1024, false>(bits, stages); break; \
+    default: break;                                                                   \
   }
 
-// Launchers used by api.cpp. Return hipErrorInvalidValue for an unsupported (d, bits,
+// Launchers used by api.cpp (d the head dimension, a multiple of 8 in [8, 1024]; the kernels
+// run at its rotation length). Return hipErrorInvalidValue for an unsupported (d, bits,
 // stages) or more than 2^31 - 1 tiles.
 hipError_t launch_encode(const EncodeArgs& a, int d, int bits, int stages, hipStream_t stream) {
   hipError_t (*f)(const EncodeArgs&, hipStream_t) = nullptr;
-  KVQ_FOR_D(encode_fn, bits, stages)
+  const int p = rotation_length(d);
+  if (d % 8 == 0 && a.dch == d / 8) KVQ_FOR_D(encode_fn, bits, stages, p != d)
   return f ? f(a, stream) : hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int d, int bits, int stages, hipStream_t stream) {
   hipError_t (*f)(const DecodeArgs&, hipStream_t) = nullptr;
-  KVQ_FOR_D(decode_fn, bits, stages)
+  const int p = rotation_length(d);
+  if (d % 8 == 0 && a.dch == d / 8) KVQ_FOR_D(decode_fn, bits, stages, p != d)
   return f ? f(a, stream) : hipErrorInvalidValue;
 }
 

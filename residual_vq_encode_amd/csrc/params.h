@@ -29,18 +29,27 @@ constexpr int kTabEntries = kTabBuckets + 1;
 // Vectors per wave tile of the matrix-core encode (the 16 columns of its MFMA).
 constexpr int kMxTile = 16;
 
+// Rotation length of head dimension d: the power of two >= d. A head dimension that is not
+// a power of two (a multiple of 8) is rotated zero-padded to it, and its codes are those of
+// all P rotated coordinates.
+constexpr int rotation_length(int d) {
+  int p = 8;
+  while (p < d) p *= 2;
+  return p;
+}
+
 // The encode of D = 128 at 1, 2 and 4 bits runs its transform on the matrix cores; every
-// other shape takes the butterfly kernel.
+// other shape (padded ones included) takes the butterfly kernel.
 constexpr bool encode_on_matrix_cores(int d, int bits) { return d == 128 && bits != 3; }
 
 // Vectors per wave tile (the unit of work of the persistent grids, indexed with 32-bit
-// integers): the matrix-core encode takes 32; the butterfly kernels spread a vector over
-// d / min(d, 32) lanes of a 64-lane wave.
-constexpr int64_t butterfly_tile_vectors(int d) { return 64 / (d / (d < 32 ? d : 32)); }
+// integers): the matrix-core encode takes 16; the butterfly kernels spread a vector over
+// p / min(p, 32) lanes of a 64-lane wave, p the rotation length.
+constexpr int64_t butterfly_tile_vectors(int p) { return 64 / (p / (p < 32 ? p : 32)); }
 constexpr int64_t encode_tile_vectors(int d, int bits) {
-  return encode_on_matrix_cores(d, bits) ? kMxTile : butterfly_tile_vectors(d);
+  return encode_on_matrix_cores(d, bits) ? kMxTile : butterfly_tile_vectors(rotation_length(d));
 }
-constexpr int64_t decode_tile_vectors(int d) { return butterfly_tile_vectors(d); }
+constexpr int64_t decode_tile_vectors(int d) { return butterfly_tile_vectors(rotation_length(d)); }
 
 // Where token s of (b, h) lands in a cache whose token axis has capacity S_cap:
 // row(v) = (v / S) * S_cap + s_offset + v % S for the flattened input index v.
@@ -52,6 +61,7 @@ struct RowMap {
 
 struct EncodeArgs {
   const uint16_t* x;  // fp16 [n_vec, d]
+  int32_t dch;        // d / 8: 16-byte chunks of an input row (less than p / 8 when padded)
   uint32_t* p1;       // [rows, n_words]
   uint32_t* p2;
   float* norms;       // [rows]
@@ -85,9 +95,10 @@ struct DecodeArgs {
   const uint32_t* p2;
   const float* norms;  // nullptr: unit reconstructions
   uint16_t* x;         // fp16 [n_vec, d]
+  int32_t dch;         // d / 8: 16-byte chunks of an output row (less than p / 8 when padded)
   int64_t n_vec;
   RowMap map;
-  float inv_sqrt_d;
+  float inv_sqrt_d;    // 1 / sqrt(p), p the rotation length
   float ztab[256];     // c1[i1] + c2[i2] (float32 sum), index (i1 << bits) | i2
   uint32_t xmask[512]; // per-pair XOR masks flipping fp16 sign bits (the final diag(s))
 };

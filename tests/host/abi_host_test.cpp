@@ -66,8 +66,25 @@ void test_codebooks() {
     neg[d - 1] = 0;  // not a sign
     CHECK(kvq_build_codebooks(d, 2, neg.data(), &cb) == KVQ_ERR_ARG);
   }
+  // a head dimension that is a multiple of 8 but not a power of two: the tables, word count
+  // and sigma1 are those of its rotation length P (the next power of two), the signs its own
+  for (int d : {24, 40, 72, 96, 200, 576, 1016}) {
+    int p = 8;
+    while (p < d) p *= 2;
+    std::vector<int8_t> neg(d, -1);
+    for (int bits = 1; bits <= 4; ++bits) {
+      kvq_codebooks cp;
+      CHECK(kvq_build_codebooks(d, bits, neg.data(), &cb) == KVQ_OK);
+      CHECK(kvq_build_codebooks(p, bits, nullptr, &cp) == KVQ_OK);
+      const int epw = 32 / bits;
+      CHECK(cb.d == d && cb.n_words == (p + epw - 1) / epw && cb.n_words == cp.n_words);
+      CHECK(cb.sigma1 == cp.sigma1 && cb.sigma2 == cp.sigma2);
+      CHECK(std::memcmp(cb.c1, cp.c1, sizeof(cb.c1)) == 0 && std::memcmp(cb.b2, cp.b2, sizeof(cb.b2)) == 0);
+      for (int j = 0; j < KVQ_MAX_D; ++j) CHECK(((cb.sign_bits[j >> 5] >> (j & 31)) & 1u) == (j < d ? 1u : 0u));
+    }
+  }
   CHECK(kvq_build_codebooks(128, 2, nullptr, nullptr) == KVQ_ERR_ARG);
-  for (int d : {0, 4, 7, 12, 96, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
+  for (int d : {0, 4, 7, 12, 100, 1020, 1032, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
   for (int bits : {0, 5, -1}) CHECK(kvq_build_codebooks(128, bits, nullptr, &cb) == KVQ_ERR_SHAPE);
 }
 
@@ -262,8 +279,22 @@ void test_encode_decode() {
   bad.n_words = 9;
   CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
   bad = cb;
-  bad.d = 96;
+  bad.d = 100;  // not a multiple of 8
   CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_SHAPE);
+  bad.d = 64;  // its word count is not that of d = 64
+  CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
+  // a padded head dimension: the launcher gets d, and the arguments the rotation length's
+  // tables with d / 8 real chunks per row; the sign code takes powers of two only
+  kvq_codebooks c96, c96b1;
+  CHECK(kvq_build_codebooks(96, 2, nullptr, &c96) == KVQ_OK && kvq_build_codebooks(96, 1, nullptr, &c96b1) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&c96, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.enc.dch == 12 && kvq::g_stub.enc.n_vec == 30);
+  CHECK(kvq_rvq_unpack_decode(&c96, p1, p2, nr, 2, 3, 5, 0, 5, x, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.dec.dch == 12 && kvq::g_stub.dec.inv_sqrt_d == 1.0f / std::sqrt(128.0f));
+  CHECK(kvq_rabitq_encode_pack(&c96b1, x, 1, 1, 8, p1, nr, 8, 0, nullptr) == KVQ_ERR_SHAPE);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.enc.dch == 16);
+  kvq::g_stub = kvq::StubLog{};
   const int before = kvq::g_stub.encode_calls;
   CHECK(kvq_rvq_encode_pack(&cb, nullptr, 0, 3, 5, nullptr, nullptr, nullptr, 5, 0, nullptr) == KVQ_OK);  // empty
   CHECK(kvq::g_stub.encode_calls == before);
@@ -488,6 +519,9 @@ void test_attend() {
   };
   CHECK(call(&ck, &cv, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_OK);
   CHECK(call(&ck, &c3, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_SHAPE);   // different bits
+  kvq_codebooks k96, v96;  // the attention takes powers of two only
+  CHECK(kvq_build_codebooks(96, 2, nullptr, &k96) == KVQ_OK && kvq_build_codebooks(96, 2, nullptr, &v96) == KVQ_OK);
+  CHECK(call(&k96, &v96, 32, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_SHAPE);
   CHECK(call(&ck, &cv, 30, 8, 4096, 4096, 0.1f, ws, need, out) == KVQ_ERR_SHAPE);   // Hq % Hkv
   CHECK(call(&ck, &cv, 32, 8, 4095, 4096, 0.1f, ws, need, out) == KVQ_ERR_RANGE);   // S_kv > S_cap
   CHECK(call(&ck, &cv, 32, 8, 4096, 0, 0.1f, ws, need, out) == KVQ_ERR_RANGE);      // S_kv < 1

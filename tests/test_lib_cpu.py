@@ -107,8 +107,10 @@ def test_host_side_argument_checks():
     broken.n_words = 7
     assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -1
     broken = kvq.Codebooks.from_buffer_copy(cb)
-    broken.d = 96
+    broken.d = 100  # not a multiple of 8
     assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -2
+    broken.d = 64   # the word count of d = 128
+    assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -1
     # shapes and ranges
     assert _enc(pcb, A, -1, 1, 1, A, A, A, 1, 0) == -2
     assert _enc(pcb, A, 1, 1, 5, A, A, A, 4, 0) == -4        # S > S_cap
