@@ -463,7 +463,11 @@ constexpr uint64_t kWalsh8 = 0x963C5AF066CCAA00ull;
 // fields of one packed word (BITS = 4) or a quarter or half of one (BITS = 1, 2); a 4 x 4
 // transpose of those pieces across the four lane groups (v_permlane32_swap, then
 // v_permlane16_swap) leaves lane group g with the vector's words [g NW / 4, (g + 1) NW / 4),
-// stored as one contiguous run.
+// stored as one contiguous run. At BITS = 3 a piece is 24 bits and the transpose leaves lane
+// group g with the 96-bit slice of the code stream that holds codes [32 g, 32 g + 32); the
+// 30-bit words (10 codes and 2 spare bits each) are cut from the slices as in the butterfly
+// kernel, and a contiguous cache receives each tile's 208 words per stream through LDS as
+// one run of 16-byte stores.
 template <int BITS, bool CONTIG, int STAGES>
 __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_kernel(const EncodeArgs a) {
   constexpr int D = 128;
@@ -472,14 +476,19 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
   constexpr int TV = kMxTile;            // vectors per tile: the MFMA's 16 columns
   constexpr int TCH = TV * CPV;          // chunks per tile
   constexpr int EPW = 32 / BITS;         // codes per word
-  constexpr int NW = D / EPW;            // words per vector per stream
-  constexpr int WPL = NW / 4;            // words each lane group stores per stream
+  constexpr int NW = (D + EPW - 1) / EPW;  // words per vector per stream
+  constexpr bool B3 = BITS == 3;         // 10-code words straddle the lane groups' slices
+  constexpr int WPL = B3 ? 4 : NW / 4;   // words each lane group holds per stream (B3: 3 or 4)
   constexpr bool TWO = STAGES == 2;
+  constexpr int NSTREAM = TWO ? 2 : 1;
+  constexpr int TW = TV * NW;            // words of a tile per stream
+  constexpr bool RUN = B3 && CONTIG;     // B3 words to a contiguous cache: one run through LDS
   static_assert(TV == 16 && NB == 4, "16 vectors of 4 blocks: one MFMA column per vector, one lane group per block");
-  static_assert(BITS == 1 || BITS == 2 || BITS == 4, "codes that tile a word");
   static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
+  static_assert(!RUN || (TW % 4 == 0 && TW / 4 <= 64), "a tile's run is at most one 16-byte chunk per lane");
 
   __shared__ u32x4_t stage[kWavesPerBlock][TCH];
+  __shared__ uint32_t pk[RUN ? kWavesPerBlock : 1][RUN ? NSTREAM * TW : 1];
   constexpr int TSLOTS = BITS >= 3 ? 128 : 1;
   __shared__ float4 t1s[TSLOTS];
   __shared__ float2 t2s[TSLOTS];
@@ -497,6 +506,10 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int v = lane & 15;  // this lane's vector in the tile
   const int g = lane >> 4;  // its lane group: input coordinates 32 k + 8 g + [0, 8)
+  // B3: the slice of lane group g is stream bits [96 g, 96 g + 96); its first word starts
+  // s_off bits in (word s_word), and it holds 4 word starts when s_off = 0 (g = 0), else 3
+  const int s_off = B3 ? (30 - (96 * g) % 30) % 30 : 0;
+  const int s_word = B3 ? (96 * g + s_off) / 30 : 0;
   u32x4_t* buf = stage[wv];
   const int n_tiles = static_cast<int>((a.n_vec + TV - 1) / TV);  // fits (checked on the host)
   const int stride = static_cast<int>(gridDim.x) * kWavesPerBlock;
@@ -550,11 +563,50 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
   uint32_t o1[WPL], o2[WPL];
   float n_prev = 0.f;
   int64_t row_prev = -1;  // -1: nothing to store (first tile, or a lane past the last vector)
+  int64_t v0_prev = -1;   // RUN: the previous tile's first vector (-1: none) and its count
+  int nv_prev = 0;
   auto store_prev = [&]() {
-    if (row_prev >= 0) {
+    if constexpr (RUN) {
+      if (row_prev >= 0 && g == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
+      if (v0_prev < 0) return;  // wave-uniform
+      uint32_t* pw = pk[wv];
+      if (row_prev >= 0) {
+        const int base = v * NW + s_word;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (k < 3 || s_off == 0) {
+            pw[base + k] = o1[k];
+            if constexpr (TWO) pw[TW + base + k] = o2[k];
+          }
+        }
+      }
+      wave_lds_fence();
+      const int valid = nv_prev * NW;  // words of the run that belong to vectors
+#pragma unroll
+      for (int st = 0; st < NSTREAM; ++st) {
+        uint32_t* dst = (st == 0 ? a.p1 : a.p2) + v0_prev * NW;
+        if (4 * lane + 4 <= valid) {
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(pw + st * TW + 4 * lane);
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(dst) + lane);
+        } else if (4 * lane < valid) {
+          for (int e = 4 * lane; e < valid; ++e) __builtin_nontemporal_store(pw[st * TW + e], dst + e);
+        }
+      }
+      wave_lds_fence();  // the reads above complete before the next tile's words land
+    } else if (row_prev >= 0) {
       if (g == 0) __builtin_nontemporal_store(n_prev, a.norms + row_prev);
-      store_words<WPL>(a.p1 + row_prev * NW + g * WPL, o1);
-      if constexpr (TWO) store_words<WPL>(a.p2 + row_prev * NW + g * WPL, o2);
+      if constexpr (B3) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (k < 3 || s_off == 0) {
+            __builtin_nontemporal_store(o1[k], a.p1 + row_prev * NW + s_word + k);
+            if constexpr (TWO) __builtin_nontemporal_store(o2[k], a.p2 + row_prev * NW + s_word + k);
+          }
+        }
+      } else {
+        store_words<WPL>(a.p1 + row_prev * NW + g * WPL, o1);
+        if constexpr (TWO) store_words<WPL>(a.p2 + row_prev * NW + g * WPL, o2);
+      }
     }
   };
 
@@ -665,6 +717,22 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
       if constexpr (BITS == 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = w[j];
+      } else if constexpr (BITS == 3) {
+        // the 96-bit slice as three dwords, then the 30-bit words starting in it (the last
+        // one reads on into the next group's slice; zero past the vector's end)
+        const uint32_t d0 = w[0] | (w[1] << 24);
+        const uint32_t d1 = (w[1] >> 8) | (w[2] << 16);
+        const uint32_t d2 = (w[2] >> 16) | (w[3] << 8);
+        uint32_t nb = static_cast<uint32_t>(__shfl(static_cast<int>(d0), lane + 16));
+        if (g == NB - 1) nb = 0u;
+        constexpr uint32_t M30 = 0x3FFFFFFFu;
+        const uint32_t at0 = s_off == 0 ? 0xFFFFFFFFu : 0u;  // a bit-select, not a branch
+        o[0] = __builtin_amdgcn_alignbit(d1, d0, s_off) & M30;
+        o[1] = ((__builtin_amdgcn_alignbit(d1, d0, 30) & at0) |
+                (__builtin_amdgcn_alignbit(d2, d1, s_off - 2) & ~at0)) & M30;
+        o[2] = ((__builtin_amdgcn_alignbit(d2, d1, 28) & at0) |
+                (__builtin_amdgcn_alignbit(nb, d2, s_off - 4) & ~at0)) & M30;
+        o[3] = __builtin_amdgcn_alignbit(nb, d2, 26) & M30;  // stored only when s_off == 0
       } else if constexpr (BITS == 2) {
         o[0] = w[0] | (w[1] << 16);
         o[1] = w[2] | (w[3] << 16);
@@ -680,6 +748,8 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
       const int64_t r = cache_row<CONTIG>(a.map, v0, v);
       row_prev = (v < nv) ? r : -1;
     }
+    v0_prev = v0;
+    nv_prev = nv;
   }
   store_prev();
 }

@@ -38,9 +38,9 @@ constexpr int rotation_length(int d) {
   return p;
 }
 
-// The encode of D = 128 at 1, 2 and 4 bits runs its transform on the matrix cores; every
+// The encode of D = 128 runs its transform on the matrix cores (every bit width); every
 // other shape (padded ones included) takes the butterfly kernel.
-constexpr bool encode_on_matrix_cores(int d, int bits) { return d == 128 && bits != 3; }
+constexpr bool encode_on_matrix_cores(int d, int bits) { return d == 128 && bits >= 1; }
 
 // Vectors per wave tile (the unit of work of the persistent grids, indexed with 32-bit
 // integers): the matrix-core encode takes 16; the butterfly kernels spread a vector over
