@@ -151,6 +151,10 @@ def gpu_idle_check() -> dict:
         try:
             import re
             import subprocess
+            if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+                # under a profiler every child process starts with its library preloaded (and the
+                # GPU initialised), and rocm-smi's launcher hop would then replace such a process
+                raise RuntimeError("skipped under a profiler")
             r = subprocess.run(["rocm-smi", "--showpids"], capture_output=True, text=True, timeout=20)
             pids = [int(m) for m in re.findall(r"^\s*(\d+)\s+\S+", r.stdout, re.M)]
             out["other_gpu_processes"] = sorted(p for p in pids if p != os.getpid()) if r.returncode == 0 else None

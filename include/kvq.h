@@ -32,7 +32,7 @@ extern "C" {
 typedef enum kvq_status {
   KVQ_OK = 0,
   KVQ_ERR_ARG = -1,    /* a required pointer is NULL, or a codebook struct is inconsistent */
-  KVQ_ERR_SHAPE = -2,  /* d not a multiple of 8 in [8, 1024] (a power of two where stated); bits not in 1..4; B, H, S < 0 */
+  KVQ_ERR_SHAPE = -2,  /* d outside [8, 1024] (or not a power of two where stated); bits not in 1..4; B, H, S < 0 */
   KVQ_ERR_ALIGN = -3,  /* an fp16 or packed-word buffer not 16-byte aligned, or a norm buffer not 4-byte aligned */
   KVQ_ERR_RANGE = -4,  /* s_offset < 0, s_offset + S > S_cap, or a size overflows 64 bits */
   KVQ_ERR_DEVICE = -5  /* the HIP launch reported an error */
@@ -47,8 +47,8 @@ typedef enum kvq_status {
  * with kvq_build_codebooks and treat it as read-only.
  *
  * The rotation length P is d rounded up to a power of two (P = d when d is one). The
- * Walsh-Hadamard transform exists at powers of two only, so a head dimension such as 96 or
- * 576 is rotated as the vector padded with P - d zeros, and all P rotated coordinates are
+ * Walsh-Hadamard transform exists at powers of two only, so a head dimension such as 96, 100
+ * or 576 is rotated as the vector padded with P - d zeros, and all P rotated coordinates are
  * coded (the zeros add nothing to the norm, and the rotated vector keeps unit norm).
  *
  * c1/b1: stage-1 centroids (2^bits, ascending) and boundaries (2^bits - 1): the
@@ -79,7 +79,7 @@ typedef struct kvq_codebooks {
 
 /*
  * kvq_build_codebooks - host only, no device calls.
- *   d     head dimension, a multiple of 8 in [8, 1024]
+ *   d     head dimension in [8, 1024]
  *   bits  bits per code per stage, 1..4
  *   signs host array of d entries, each +1 or -1 (the rotation's sign vector), or NULL
  *         for all +1

@@ -13,7 +13,7 @@ What the pages fix (VeloxQuant-MLX blog):
 Readings taken where the pages are silent:
   * Stage 1 is the 2**b-level Lloyd-Max quantizer of N(0, sigma1**2) with sigma1**2 = 1/P,
     the per-coordinate variance of a rotated unit vector of P coordinates. P = D for a
-    power-of-two head dimension; any other D (a multiple of 8) is rotated zero-padded to the
+    power-of-two head dimension; any other D in [8, 1024] is rotated zero-padded to the
     next power of two P (see rvq.py), so its tables are those of P.
   * Stage 2 is the 2**b-level Lloyd-Max quantizer of a zero-mean Laplace density whose
     variance equals the stage-1 mean squared error, sigma2**2 = MSE_G(b) * sigma1**2,

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Per head vector x (fp16, length D), following the VeloxQuant-MLX blog. A head dimension D
-that is not a power of two (a multiple of 8) is taken as the vector zero-padded to
+that is not a power of two (any D in [8, 1024]) is taken as the vector zero-padded to
 P = the next power of two: the norm is unchanged, the rotation below is of length P (the
 padded coordinates' signs are +1; they multiply zeros), all P rotated coordinates are
 quantized and packed, and the decode reconstructs P coordinates and returns the first D.

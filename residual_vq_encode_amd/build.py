@@ -2,7 +2,8 @@
 
     python -m residual_vq_encode_amd.build
 
-Sources: csrc/kernels.hip (codec kernels), csrc/attend.hip (attention over the packed
+Sources: csrc/kernels.hip and csrc/kernels_ragged.hip (codec kernels of csrc/codec.h, for
+head dimensions whose rows are and are not 16-byte aligned), csrc/attend.hip (attention over the packed
 cache), csrc/qjl.hip (1-bit sign-sketch encoder), csrc/api.cpp (C ABI, launches),
 csrc/codebooks.cpp (host codebook builder). Each
 is compiled to an object file in parallel (in a private temporary directory), then the
@@ -27,7 +28,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "attend.hip", "qjl.hip", "api.cpp", "codebooks.cpp"]
+SOURCES = ["kernels.hip", "kernels_ragged.hip", "attend.hip", "qjl.hip", "api.cpp", "codebooks.cpp"]
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument"]

@@ -63,7 +63,7 @@ bool stage_tables_ok(const float* c, const float* b, int bits) {
 
 kvq_status check_codebooks(const kvq_codebooks* cb) {
   if (cb == nullptr) return KVQ_ERR_ARG;
-  if (cb->d < KVQ_MIN_D || cb->d > KVQ_MAX_D || cb->d % 8 != 0) return KVQ_ERR_SHAPE;
+  if (cb->d < KVQ_MIN_D || cb->d > KVQ_MAX_D) return KVQ_ERR_SHAPE;
   if (cb->bits < 1 || cb->bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
   const int epw = 32 / cb->bits, p = kvq::rotation_length(cb->d);
   if (cb->elems_per_word != epw || cb->n_words != (p + epw - 1) / epw) return KVQ_ERR_ARG;
@@ -165,7 +165,7 @@ float as_float(int32_t v) {
 kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
   const int d = kvq::rotation_length(cb->d), bits = cb->bits;  // the rotation's length
   const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
-  a->dch = cb->d / 8;
+  a->dh = cb->d;
   std::memset(a->wpair, 0, sizeof(a->wpair));
   std::memset(a->tab1, 0, sizeof(a->tab1));
   std::memset(a->tab2, 0, sizeof(a->tab2));
@@ -210,7 +210,7 @@ kvq_status fill_encode_args(const kvq_codebooks* cb, EncodeArgs* a) {
 void fill_decode_args(const kvq_codebooks* cb, int stages, DecodeArgs* a) {
   const int d = kvq::rotation_length(cb->d), bits = cb->bits, k = 1 << bits;  // the rotation's length
   a->inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
-  a->dch = cb->d / 8;
+  a->dh = cb->d;
   std::memset(a->ztab, 0, sizeof(a->ztab));
   for (int i1 = 0; i1 < k; ++i1) {
     if (stages == 1) {

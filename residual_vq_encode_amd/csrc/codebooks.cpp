@@ -90,7 +90,7 @@ void fill_tables(int bits, const double* pos, double sigma, float* c, float* b) 
 
 extern "C" kvq_status kvq_build_codebooks(int32_t d, int32_t bits, const int8_t* signs, kvq_codebooks* out) {
   if (out == nullptr) return KVQ_ERR_ARG;
-  if (d < KVQ_MIN_D || d > KVQ_MAX_D || d % 8 != 0) return KVQ_ERR_SHAPE;
+  if (d < KVQ_MIN_D || d > KVQ_MAX_D) return KVQ_ERR_SHAPE;
   if (bits < 1 || bits > KVQ_MAX_BITS) return KVQ_ERR_SHAPE;
   if (signs != nullptr)
     for (int j = 0; j < d; ++j)
@@ -126,7 +126,7 @@ extern "C" const char* kvq_status_str(kvq_status status) {
   switch (status) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_ARG: return "invalid argument (null pointer or inconsistent codebooks)";
-    case KVQ_ERR_SHAPE: return "unsupported shape (d must be a multiple of 8 in [8,1024], bits in 1..4, sizes >= 0)";
+    case KVQ_ERR_SHAPE: return "unsupported shape (d must be in [8,1024], bits in 1..4, sizes >= 0)";
     case KVQ_ERR_ALIGN: return "misaligned buffer (fp16 and packed-word buffers need 16-byte, norm buffers 4-byte alignment)";
     case KVQ_ERR_RANGE: return "out of range (s_offset + S exceeds S_cap, or a size overflows)";
     case KVQ_ERR_DEVICE: return "HIP launch failed";

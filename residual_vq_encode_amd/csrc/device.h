@@ -263,6 +263,57 @@ __device__ __forceinline__ void dma_dense(uint4* buf, const uint4* src, int nchu
   }
 }
 
+// Direct-to-LDS loads of ndw >= 1 consecutive dwords from src (4-byte aligned) into
+// buf32[0, ndw): instruction k writes slots [64k, 64k + 64), lanes past ndw re-read the last
+// dword, so every load stays inside the input. NI instructions cover up to 64 NI dwords.
+template <int NI>
+__device__ __forceinline__ void dma_dwords(uint32_t* buf32, const uint32_t* src, int ndw, int lane) {
+  const char* base = reinterpret_cast<const char*>(src);  // wave-uniform
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    if (64 * k < ndw) {  // wave-uniform
+      const int s = k * 64 + lane;
+      const uint32_t off = static_cast<uint32_t>(s < ndw ? s : ndw - 1) * 4u;
+      __builtin_amdgcn_global_load_lds((gptr_t)(base + off), (lptr_t)(buf32 + k * 64), 4, 0, kNonTemporal);
+    }
+  }
+}
+
+// The fp16 coordinates [cq, cq + C) of vector vl of a tile of n elements (rows of dh, C even)
+// held densely in LDS as dwords by dma_dwords, as C / 2 fp16 pairs, zero from coordinate dh
+// on. The lane's first element e0 = vl dh + cq sits in the upper half of a dword when e0 is
+// odd; its pairs are then re-cut across the dword boundaries. A tile of odd n has only
+// (n - 1) / 2 dwords in LDS (the last dword would reach past the input); its last element
+// tx[n - 1] is read from HBM by the lanes that need it (tx: the tile's first element).
+// Reads past the vector's row stay inside the buffer and are masked.
+template <int C>
+__device__ __forceinline__ void ragged_pairs(const uint32_t* b32, const uint16_t* tx, int vl, int cq, int dh, int n,
+                                             uint32_t (&xr)[C / 2]) {
+#pragma unroll
+  for (int p = 0; p < C / 2; ++p) xr[p] = 0u;
+  if (cq >= dh) return;  // the lane's slice is all padding
+  const int e0 = vl * dh + cq, bi = e0 >> 1;
+  uint32_t w[C / 2 + 1];
+#pragma unroll
+  for (int k = 0; k <= C / 2; ++k) w[k] = b32[bi + k];
+  if (n & 1) {              // wave-uniform
+    const int mdw = n >> 1;  // the dword left out: its low half is element n - 1
+    if (mdw >= bi && mdw <= bi + C / 2) {
+      const uint32_t xl = tx[n - 1];
+#pragma unroll
+      for (int k = 0; k <= C / 2; ++k)
+        if (bi + k == mdw) w[k] = xl;
+    }
+  }
+  const bool odd = (e0 & 1) != 0;
+#pragma unroll
+  for (int p = 0; p < C / 2; ++p) {
+    const uint32_t pr = odd ? __builtin_amdgcn_alignbit(w[p + 1], w[p], 16) : w[p];
+    const int c = cq + 2 * p;
+    xr[p] = c + 1 < dh ? pr : (c < dh ? (pr & 0xFFFFu) : 0u);
+  }
+}
+
 // Cache row of flattened input vector v0 + i: (v / S) * S_cap + s_offset + v % S.
 // CONTIG (S == S_cap, s_offset == 0, chosen on the host) compiles to v0 + i. i < 64.
 template <bool CONTIG>

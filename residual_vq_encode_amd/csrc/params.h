@@ -30,12 +30,23 @@ constexpr int kTabEntries = kTabBuckets + 1;
 constexpr int kMxTile = 16;
 
 // Rotation length of head dimension d: the power of two >= d. A head dimension that is not
-// a power of two (a multiple of 8) is rotated zero-padded to it, and its codes are those of
-// all P rotated coordinates.
+// a power of two is rotated zero-padded to it, and its codes are those of all P rotated
+// coordinates.
 constexpr int rotation_length(int d) {
   int p = 8;
   while (p < d) p *= 2;
   return p;
+}
+
+// How the fp16 rows of head dimension d sit against the rotation length p the kernels run
+// at: d = p (kRowsFull); d a multiple of 8 below p, rows of d / 8 16-byte chunks
+// (kRowsChunks); any other d, rows of d elements that are not 16-byte aligned (kRowsRagged).
+// Either way the p - d missing coordinates are the zeros of the padded vector.
+constexpr int kRowsFull = 0;
+constexpr int kRowsChunks = 1;
+constexpr int kRowsRagged = 2;
+constexpr int row_mode(int d) {
+  return d == rotation_length(d) ? kRowsFull : (d % 8 == 0 ? kRowsChunks : kRowsRagged);
 }
 
 // The encode of D = 128 runs its transform on the matrix cores (every bit width); every
@@ -61,7 +72,7 @@ struct RowMap {
 
 struct EncodeArgs {
   const uint16_t* x;  // fp16 [n_vec, d]
-  int32_t dch;        // d / 8: 16-byte chunks of an input row (less than p / 8 when padded)
+  int32_t dh;         // head dimension d: fp16 elements of an input row (at most p)
   uint32_t* p1;       // [rows, n_words]
   uint32_t* p2;
   float* norms;       // [rows]
@@ -95,7 +106,7 @@ struct DecodeArgs {
   const uint32_t* p2;
   const float* norms;  // nullptr: unit reconstructions
   uint16_t* x;         // fp16 [n_vec, d]
-  int32_t dch;         // d / 8: 16-byte chunks of an output row (less than p / 8 when padded)
+  int32_t dh;          // head dimension d: fp16 elements of an output row (at most p)
   int64_t n_vec;
   RowMap map;
   float inv_sqrt_d;    // 1 / sqrt(p), p the rotation length

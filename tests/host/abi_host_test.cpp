@@ -66,9 +66,9 @@ void test_codebooks() {
     neg[d - 1] = 0;  // not a sign
     CHECK(kvq_build_codebooks(d, 2, neg.data(), &cb) == KVQ_ERR_ARG);
   }
-  // a head dimension that is a multiple of 8 but not a power of two: the tables, word count
-  // and sigma1 are those of its rotation length P (the next power of two), the signs its own
-  for (int d : {24, 40, 72, 96, 200, 576, 1016}) {
+  // a head dimension that is not a power of two: the tables, word count and sigma1 are those
+  // of its rotation length P (the next power of two), the signs its own
+  for (int d : {9, 13, 24, 40, 72, 96, 100, 200, 576, 1016, 1023}) {
     int p = 8;
     while (p < d) p *= 2;
     std::vector<int8_t> neg(d, -1);
@@ -84,7 +84,7 @@ void test_codebooks() {
     }
   }
   CHECK(kvq_build_codebooks(128, 2, nullptr, nullptr) == KVQ_ERR_ARG);
-  for (int d : {0, 4, 7, 12, 100, 1020, 1032, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
+  for (int d : {-8, 0, 4, 7, 1025, 1032, 2048}) CHECK(kvq_build_codebooks(d, 2, nullptr, &cb) == KVQ_ERR_SHAPE);
   for (int bits : {0, 5, -1}) CHECK(kvq_build_codebooks(128, bits, nullptr, &cb) == KVQ_ERR_SHAPE);
 }
 
@@ -279,7 +279,7 @@ void test_encode_decode() {
   bad.n_words = 9;
   CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
   bad = cb;
-  bad.d = 100;  // not a multiple of 8
+  bad.d = 1025;  // above the largest head dimension
   CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_SHAPE);
   bad.d = 64;  // its word count is not that of d = 64
   CHECK(kvq_rvq_encode_pack(&bad, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_ERR_ARG);
@@ -288,12 +288,16 @@ void test_encode_decode() {
   kvq_codebooks c96, c96b1;
   CHECK(kvq_build_codebooks(96, 2, nullptr, &c96) == KVQ_OK && kvq_build_codebooks(96, 1, nullptr, &c96b1) == KVQ_OK);
   CHECK(kvq_rvq_encode_pack(&c96, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
-  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.enc.dch == 12 && kvq::g_stub.enc.n_vec == 30);
+  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.enc.dh == 96 && kvq::g_stub.enc.n_vec == 30);
   CHECK(kvq_rvq_unpack_decode(&c96, p1, p2, nr, 2, 3, 5, 0, 5, x, nullptr) == KVQ_OK);
-  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.dec.dch == 12 && kvq::g_stub.dec.inv_sqrt_d == 1.0f / std::sqrt(128.0f));
+  CHECK(kvq::g_stub.d == 96 && kvq::g_stub.dec.dh == 96 && kvq::g_stub.dec.inv_sqrt_d == 1.0f / std::sqrt(128.0f));
   CHECK(kvq_rabitq_encode_pack(&c96b1, x, 1, 1, 8, p1, nr, 8, 0, nullptr) == KVQ_ERR_SHAPE);
+  kvq_codebooks c100;  // rows that are not 16-byte aligned: the same arguments, d elements a row
+  CHECK(kvq_build_codebooks(100, 3, nullptr, &c100) == KVQ_OK && c100.n_words == 13);
+  CHECK(kvq_rvq_encode_pack(&c100, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
+  CHECK(kvq::g_stub.d == 100 && kvq::g_stub.enc.dh == 100);
   CHECK(kvq_rvq_encode_pack(&cb, x, 2, 3, 5, p1, p2, nr, 5, 0, nullptr) == KVQ_OK);
-  CHECK(kvq::g_stub.enc.dch == 16);
+  CHECK(kvq::g_stub.enc.dh == 128);
   kvq::g_stub = kvq::StubLog{};
   const int before = kvq::g_stub.encode_calls;
   CHECK(kvq_rvq_encode_pack(&cb, nullptr, 0, 3, 5, nullptr, nullptr, nullptr, 5, 0, nullptr) == KVQ_OK);  // empty

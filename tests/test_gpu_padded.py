@@ -1,4 +1,4 @@
-"""GPU parity for head dimensions that are not powers of two (multiples of 8 in [8, 1024]).
+"""GPU parity for head dimensions that are not powers of two (any d in [8, 1024]).
 
 The Walsh-Hadamard rotation exists at powers of two only ("rvq" tag page, "The pipeline, as
 it actually runs": normalise, then rotate by the sign-flipped Hadamard transform); such a
@@ -20,8 +20,12 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-# rotation lengths 32 (24), 64 (40), 128 (80, 96, 120), 256 (192, 200), 1024 (576, 1016)
+# Multiples of 8, whose rows are whole 16-byte chunks: rotation lengths 32 (24), 64 (40),
+# 128 (80, 96, 120), 256 (192, 200), 1024 (576, 1016). Any other d, whose rows are moved as
+# dwords and may start in the middle of one: 16 (9, 12), 32 (20), 64 (33), 128 (100, 127),
+# 256 (130), 512 (257), 1024 (514, 1023).
 D_PAD = [24, 40, 80, 96, 120, 192, 200, 576, 1016]
+D_RAGGED = [9, 12, 20, 33, 100, 127, 130, 257, 514, 1023]
 
 
 def _say(msg):
@@ -32,7 +36,7 @@ def _signs(seed, d):
     return synth.signs(seed, d).numpy()
 
 
-@pytest.mark.parametrize("d", D_PAD)
+@pytest.mark.parametrize("d", D_PAD + D_RAGGED)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("n", [1, 37, 3001])
 def test_padded_encode_decode(d, bits, n):
@@ -49,7 +53,7 @@ def test_padded_encode_decode(d, bits, n):
     gu.check_decode_from_oracle_words(ref, s, bits, tuple(x.shape))
 
 
-@pytest.mark.parametrize("d", D_PAD)
+@pytest.mark.parametrize("d", D_PAD + D_RAGGED)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_padded_single_stage(d, bits):
     _say(f"padded single stage d={d} bits={bits}")
@@ -73,7 +77,7 @@ def _degenerate_rows(d):
     return np.stack(rows).astype(np.float16)
 
 
-@pytest.mark.parametrize("d", [24, 96, 576])
+@pytest.mark.parametrize("d", [24, 96, 576, 9, 127, 1023])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_padded_degenerate(d, bits):
     """Zero, constant, one-hot (at the first and last real coordinates too), extreme and
@@ -85,7 +89,7 @@ def test_padded_degenerate(d, bits):
     gu.check_decode_from_oracle_words(ref, s, bits, tuple(x.shape))
 
 
-@pytest.mark.parametrize("d", [24, 96, 192, 576])
+@pytest.mark.parametrize("d", [24, 96, 192, 576, 9, 100, 127, 1023])
 @pytest.mark.parametrize("S,S_cap,s_offset", [(1, 9, 4), (70, 200, 13)])
 def test_padded_cache_window(d, S, S_cap, s_offset):
     """Writes into a window of a larger cache (the row-mapped kernels), positions outside it
@@ -109,18 +113,21 @@ def test_padded_cache_window(d, S, S_cap, s_offset):
     c2 = torch.zeros_like(p2)
     c1[:, :, win] = torch.from_numpy(ref["packed1"].view(np.int32)).reshape(2, 3, S, nw).to(DEV)
     c2[:, :, win] = torch.from_numpy(ref["packed2"].view(np.int32)).reshape(2, 3, S, nw).to(DEV)
-    # the output sits between guard rows: a store past the last real chunk of a row shows
-    guard = torch.full(((2 * 3 * S + 2) * d,), 7.0, dtype=torch.float16, device=DEV)
-    out = guard[d:-d].view(2, 3, S, d)
+    # the output sits between guard elements (16 bytes on either side, so that it stays
+    # 16-byte aligned): a store past the last real element of a row or of the run shows
+    ne = 2 * 3 * S * d
+    guard = torch.full((ne + 16,), 7.0, dtype=torch.float16, device=DEV)
+    out = guard[8:8 + ne].view(2, 3, S, d)
     kvq.kvq_rvq_unpack_decode(cb, c1, c2, None, out, s_offset=s_offset)
     torch.cuda.synchronize()
     want = rvq.decode(ref["packed1"], ref["packed2"], None, s, gu.tables(d, bits)).astype(np.float64)
     assert np.max(np.abs(out.cpu().numpy().reshape(-1, d).astype(np.float64) - want)) <= gu.DECODE_UNIT_ATOL
-    assert bool((guard[:d] == 7.0).all()) and bool((guard[-d:] == 7.0).all())
+    assert bool((guard[:8] == 7.0).all()) and bool((guard[8 + ne:] == 7.0).all())
 
 
 @pytest.mark.parametrize("d,shape", [(96, (2, 8, 4096)), (80, (1, 8, 4099)), (576, (1, 4, 2048)),
-                                     (192, (1, 8, 4096))])
+                                     (192, (1, 8, 4096)), (100, (2, 8, 4096)), (127, (1, 8, 4099)),
+                                     (1023, (1, 4, 2047))])
 @pytest.mark.parametrize("bits", [2, 4])
 def test_padded_every_vector_at_scale(d, shape, bits):
     """Larger launches (several rounds of the persistent grid): every vector judged, and

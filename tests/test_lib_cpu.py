@@ -76,8 +76,10 @@ def test_codebooks_match_oracle_bit_exactly(d, bits):
 def test_build_codebooks_rejects():
     lib = kvq.load()
     cb = kvq.Codebooks()
-    for d in (0, 4, 12, 2048, -8):
+    for d in (0, 4, 7, 1025, 2048, -8):
         assert lib.kvq_build_codebooks(d, 2, None, ctypes.byref(cb)) == -2
+    for d in (8, 9, 12, 100, 1023, 1024):  # any head dimension in [8, 1024]
+        assert lib.kvq_build_codebooks(d, 2, None, ctypes.byref(cb)) == 0 and cb.n_words == kvq.n_words(d, 2)
     for b in (0, 5, -1):
         assert lib.kvq_build_codebooks(128, b, None, ctypes.byref(cb)) == -2
     assert lib.kvq_build_codebooks(128, 2, None, None) == -1
@@ -107,7 +109,7 @@ def test_host_side_argument_checks():
     broken.n_words = 7
     assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -1
     broken = kvq.Codebooks.from_buffer_copy(cb)
-    broken.d = 100  # not a multiple of 8
+    broken.d = 1025  # above the largest head dimension
     assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -2
     broken.d = 64   # the word count of d = 128
     assert _enc(ctypes.byref(broken), A, 1, 1, 1, A, A, A, 1, 0) == -1

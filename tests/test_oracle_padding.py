@@ -17,7 +17,7 @@ from scipy.linalg import hadamard
 from oracle import codebooks as cb
 from oracle import packing, rvq
 
-D_PAD = [24, 40, 80, 96, 192, 576]
+D_PAD = [24, 40, 80, 96, 192, 576, 9, 13, 100, 127, 1023]  # multiples of 8 and not
 
 
 def _x(d, n, seed):
