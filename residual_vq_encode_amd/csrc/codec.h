@@ -10,26 +10,30 @@
 // c1[i1] + c2[i2]).
 //
 // The pages' Metal kernel runs one threadgroup per vector and one thread per coordinate,
-// stages codes in threadgroup memory and packs them after a barrier. Here a vector of D
-// coordinates is spread over L = D / C lanes of a 64-wide wavefront, C = min(D, 32)
-// consecutive coordinates per lane, so a wave works on 64 / L vectors at a time (a tile):
-//  * the tile (64 * C fp16 values, contiguous in HBM) is streamed into the wave's own LDS
-//    buffer with coalesced 16-byte direct-to-LDS loads (global_load_lds_dwordx4); each lane
-//    reads its C coordinates back. The 16-byte chunks are XOR-swizzled so those reads are
-//    bank-conflict free. The next tile's loads are issued as soon as the current tile has
-//    left LDS, so they fly while the current tile is computed;
-//  * the Walsh-Hadamard transform runs its log2 C low stages in registers and its log2 L
-//    high stages across lanes (DPP quad permutes / row rotates, or ds_swizzle), each
-//    butterfly output one instruction (see cross_stage). The sign flip diag(s) is an exact
-//    XOR of fp16 sign bits; the first two stages read the flipped fp16 pairs directly
-//    (v_dot2 with (1, 1) and (1, -1) weights: one instruction per output, exact products);
+// stages codes in threadgroup memory and packs them after a barrier. Here:
+//  * at D = 128 (encode_mx_kernel) a wave takes 16 vectors at a time and runs the transform
+//    on the matrix cores as H_4 (x) H_32: eight v_mfma_f32_16x16x32_f16 products of an
+//    fp16 +-1 H_32 slice with the sign-flipped fp16 inputs (exact products, float32 sums)
+//    and two float32 butterfly stages across the 32-coordinate blocks; each lane then
+//    quantizes 8 coordinates of every output block, and a 4 x 4 transpose of the code
+//    pieces across lane groups (v_permlane32_swap, v_permlane16_swap) gives each lane group
+//    a contiguous quarter of the vector's words;
+//  * at every other D (encode_kernel) a vector of P coordinates (P = D, or the next power
+//    of two for other head dimensions) is spread over L = P / C lanes of a 64-wide
+//    wavefront, C = min(P, 32) consecutive coordinates per lane, and the Walsh-Hadamard
+//    transform runs its log2 C low stages in registers and its log2 L high stages across
+//    lanes (DPP quad permutes / row rotates, or ds_swizzle), each butterfly output one
+//    instruction (see cross_stage); the sign flip diag(s) is exact, folded into the fp16
+//    weights of the first two stages (v_dot2 with (+-1, +-1) weights, exact products);
+//  * in both, a tile is streamed into the wave's own LDS buffer with coalesced 16-byte
+//    direct-to-LDS loads (dwords for rows that are not 16-byte aligned), XOR-swizzled so
+//    the lanes' reads back are bank-conflict free, and the next tile's loads are issued as
+//    soon as the current tile has left LDS, so they fly while it is computed;
 //  * quantization is branch-free; codes are shifted into their words with v_alignbit /
-//    shift-or as they are produced, so no code leaves registers (3-bit codes, whose 10-code
-//    words straddle lanes, are regrouped through LDS).
-// Small per-lane state (32 coordinates) keeps many waves resident per SIMD, and a tile is
-// short, so loads of some waves overlap the arithmetic of others and the launch has little
-// tail. No MFMA: the transform is O(D log D) additions with +-1 coefficients, and the
-// kernel is bound by HBM bandwidth, not by a dense contraction.
+//    shift-or as they are produced (3-bit codes, whose 10-code words straddle lanes, are
+//    cut from 96-bit slices and, for a contiguous cache, written back through LDS as one
+//    run of 16-byte stores).
+// The grids are persistent: every wave stays resident and walks tiles with a grid stride.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,4 +1,4 @@
-// Device-side building blocks shared by the codec kernels (kernels.hip) and the
+// Device-side building blocks shared by the codec kernels (codec.h) and the
 // attention kernels over the packed cache (attend.hip): the lane layout of a head vector,
 // the Walsh-Hadamard butterfly in registers and across lanes, the direct-to-LDS tile load,
 // cache-row arithmetic, word loads and stores, and the 3-bit code regrouping helpers.
