@@ -985,8 +985,9 @@ static bool residency(const void* f, int* cus, int* per_cu) {
 // last round's arithmetic on the busiest SIMD. With balance set, the grid takes the number
 // of resident blocks per CU (from the most that fit down to 2) whose last round puts the
 // fewest waves on one SIMD (a block's waves sit on the four SIMDs of its CU), preferring
-// more blocks on ties: 16384 tiles on 256 CUs run as 3 blocks per CU (5 rounds of 3072
-// waves and a last round of 1024, one wave per SIMD) rather than 4 (4 full rounds).
+// more blocks on ties: the matrix-core encode's 16384 tiles on 256 CUs run as 3 blocks per
+// CU (5 rounds of 3072 waves and a last round of 1024, one wave per SIMD) rather than 4
+// (4 full rounds), and the decode's 16384 tiles as 5 of its 8 resident blocks per CU.
 static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* cap, bool balance,
                          hipStream_t stream) {
   const int64_t tiles = (n_vec + vw - 1) / vw;
@@ -1025,7 +1026,7 @@ static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   } else {
     const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES, ROWS>)
                       : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES, ROWS>);
-    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
+    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], true, stream);
   }
 }
 
@@ -1035,7 +1036,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const bool c = a.map.contiguous != 0;
   const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES, ROWS>)
                     : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES, ROWS>);
-  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
+  // the tail-balanced grid (see launch) at 2 to 4 bits: 16.5 against 18.0 us at b = 2, 19.5
+  // against 20.5 at b = 4 and 20.2 against 23.8 at b = 3 on the Llama layer's caches; at
+  // 1 bit every resident wave (13.1 against 13.5 us)
+  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], BITS >= 2, stream);
 }
 
 }  // namespace kvq
