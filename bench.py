@@ -139,6 +139,8 @@ def prime(stream) -> None:
     kernels back to back rather than the host's catch-up. The spin itself is outside the
     events."""
     import torch
+    if not hasattr(torch.cuda, "_sleep"):  # a torch without the spin kernel: no priming
+        return
     with torch.cuda.stream(stream):
         torch.cuda._sleep(PRIME_CYCLES)
 
