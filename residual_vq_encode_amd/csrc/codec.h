@@ -987,7 +987,8 @@ static bool residency(const void* f, int* cus, int* per_cu) {
 // fewest waves on one SIMD (a block's waves sit on the four SIMDs of its CU), preferring
 // more blocks on ties: the matrix-core encode's 16384 tiles on 256 CUs run as 3 blocks per
 // CU (5 rounds of 3072 waves and a last round of 1024, one wave per SIMD) rather than 4
-// (4 full rounds), and the decode's 16384 tiles as 5 of its 8 resident blocks per CU.
+// (4 full rounds). The decodes keep every resident block: their last round is short and
+// the writes of the others' tiles hide it.
 static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* cap, bool balance,
                          hipStream_t stream) {
   const int64_t tiles = (n_vec + vw - 1) / vw;
@@ -1036,10 +1037,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const bool c = a.map.contiguous != 0;
   const void* f = c ? reinterpret_cast<const void*>(&decode_kernel<D, BITS, true, STAGES, ROWS>)
                     : reinterpret_cast<const void*>(&decode_kernel<D, BITS, false, STAGES, ROWS>);
-  // the tail-balanced grid (see launch) at 2 to 4 bits: 16.5 against 18.0 us at b = 2, 19.5
-  // against 20.5 at b = 4 and 20.2 against 23.8 at b = 3 on the Llama layer's caches; at
-  // 1 bit every resident wave (13.1 against 13.5 us)
-  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], BITS >= 2, stream);
+  return launch(f, const_cast<DecodeArgs*>(&a), a.n_vec, Layout<D>::VW, cap[c ? 1 : 0], false, stream);
 }
 
 }  // namespace kvq
