@@ -145,6 +145,15 @@ def prime(stream) -> None:
         torch.cuda._sleep(PRIME_CYCLES)
 
 
+def output_sets(pool: int, set_bytes: int) -> int:
+    """Number of output buffer sets an encode rotates through: the smallest multiple of the
+    input pool whose bytes exceed twice the last-level cache (at most 128 sets), so a
+    launch's writes never land in lines an earlier launch left in that cache, and encode k
+    always pairs input k mod pool with output set k."""
+    need = -(-(2 * LLC_BYTES + 1) // set_bytes)
+    return pool * max(1, min(max(1, 128 // pool), -(-need // pool)))
+
+
 def block_size(steps: int) -> int:
     """Launches per timed block: 10, or fewer so that even a short run has 4 blocks (the A/A
     noise floor compares even and odd blocks)."""
@@ -442,15 +451,18 @@ def main() -> int:
     xs = [synth.tensor(spec, device=dev)]
     for i in range(1, P):
         xs.append(synth.tensor(synth.TensorSpec(B, H, S, D, spec.kind, spec.seed + 1000 * i), device=dev))
-    p1s = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(P)]
-    p2s = [torch.empty_like(p1s[0]) for _ in range(P)]
-    ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(P)]
+    # The encodes write their own pool of packed outputs, more than twice the 256 MB
+    # last-level cache, so their writes go to HBM rather than to lines still held there.
+    packed_bytes = B * H * S * (stages * nw * 4 + 4)
+    PO = output_sets(P, packed_bytes)
+    p1s = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(PO)]
+    p2s = [torch.empty_like(p1s[0]) for _ in range(PO)]
+    ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(PO)]
     outs = [torch.empty((B, H, S, D), dtype=torch.float16, device=dev) for _ in range(P)]
     stream = torch.cuda.current_stream()
     # The decodes read their own pool of packed caches, more than twice the 256 MB last-level
     # cache, each written by an encode before the timed region: a decode's input then comes
     # from HBM, not from the caches the encode blocks have just written.
-    packed_bytes = B * H * S * (stages * nw * 4 + 4)
     PD = min(64, max(P, -(-(2 * LLC_BYTES + 1) // packed_bytes)))
     dq1 = [torch.empty_like(p1s[0]) for _ in range(PD)]
     dq2 = [torch.empty_like(p1s[0]) for _ in range(PD)] if stages == 2 else None
@@ -467,15 +479,15 @@ def main() -> int:
     # Launches are prepared once (arguments checked and marshalled by the binding), so the
     # timed loop issues them as fast as the host can call the C ABI and the events measure
     # the GPU rather than per-call Python checks.
-    encs = [kvq.prepare_encode(cb, xs[j], p1s[j], p2s[j] if stages == 2 else None, ns[j], 0, stream, stages)
-            for j in range(P)]
+    encs = [kvq.prepare_encode(cb, xs[k % P], p1s[k], p2s[k] if stages == 2 else None, ns[k], 0, stream, stages)
+            for k in range(PO)]
     decs = [kvq.prepare_decode(cb, dq1[k], dq2[k] if stages == 2 else None, dqn[k], outs[k % P], 0, stream, stages)
             for k in range(PD)]
     for k in range(PD):
         kvq.prepare_encode(cb, xs[k % P], dq1[k], dq2[k] if stages == 2 else None, dqn[k], 0, stream, stages)()
 
     def enc(j):
-        encs[j]()
+        encs[j % PO]()
 
     def dec(j):
         decs[j % PD]()
@@ -484,7 +496,7 @@ def main() -> int:
     for i in range(args.warmup):
         dec(i)
     for i in range(args.warmup):
-        enc(i % P)
+        enc(i)
     torch.cuda.synchronize()
 
     # The K steps' encodes run first, then their decodes, each in blocks of back-to-back
@@ -503,7 +515,7 @@ def main() -> int:
     ev[0].record(stream)
     for bi, (a, b) in enumerate(blocks):
         for i in range(a, b):
-            enc((args.warmup + i) % P)
+            enc(args.warmup + i)
         ev[bi + 1].record(stream)
     for bi, (a, b) in enumerate(blocks):
         for i in range(a, b):
@@ -526,7 +538,8 @@ def main() -> int:
     # parity re-check of one timed output against the oracle on a sample of its vectors
     from oracle import codebooks as ocb
     from oracle import flips, rvq
-    j = (args.warmup + K - 1) % P
+    k = (args.warmup + K - 1) % PO
+    j = k % P
     # a strided sample (the whole tensor when smaller): the flip cap is a rate. At b <= 2
     # flips are rare and 65536 vectors suffice; at b >= 3 the float32 transform leaves about
     # 5e-7 of the codes flipped next to a boundary, so the sample takes 2^18 vectors (67M
@@ -535,11 +548,11 @@ def main() -> int:
     idx = torch.arange(0, n_vec, max(1, n_vec // n_check))[:n_check]
     rows = xs[j].reshape(-1, D)[idx.to(dev)].cpu().numpy()
     t = ocb.build_tables(D, bits)
-    dev_p1 = p1s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
-    dev_n = ns[j].reshape(-1)[idx.to(dev)].cpu().numpy()
+    dev_p1 = p1s[k].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
+    dev_n = ns[k].reshape(-1)[idx.to(dev)].cpu().numpy()
     if stages == 2:
         ref = rvq.encode(rows, signs, t)
-        rep = flips.compare_encode(dev_p1, p2s[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32),
+        rep = flips.compare_encode(dev_p1, p2s[k].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32),
                                    dev_n, ref, t, 1e-5)
     else:
         rep = flips.compare_encode_single(dev_p1, dev_n, rvq.encode_mse(rows, signs, t), t, 1e-5)
@@ -562,7 +575,7 @@ def main() -> int:
         "config": {"workload": f"{args.workload}: {w.note.split('; b')[0]}; b={bits}"
                                + ("" if stages == 2 else "; single-stage codec"),
                    "shape": [B, H, S, D], "bits": bits, "stages": stages,
-                   "pool_tensors": P, "step": "encode+pack then unpack+decode of one tensor"},
+                   "pool_tensors": P, "encode_output_sets": PO, "step": "encode+pack then unpack+decode of one tensor"},
         "pct_of_hbm_peak": round(100.0 * enc_gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(B * S / (enc_us * 1e-6), 1),
         "head_vectors_per_s": round(n_vec / (enc_us * 1e-6), 1),
@@ -617,24 +630,26 @@ def bench_signcodes(args, idle: dict) -> int:
         signs = synth.signs(w.sign_seed, D).numpy()
         cb = kvq.build_codebooks(D, 1, signs)
         nw = cb.n_words
-        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(P)]
-        ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(P)]
+        PO = output_sets(P, n_vec * (nw * 4 + 4))
+        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(PO)]
+        ns = [torch.empty((B, H, S), dtype=torch.float32, device=dev) for _ in range(PO)]
 
         def enc(j):
-            kvq.kvq_rabitq_encode_pack(cb, xs[j], ps[j], ns[j], 0, stream)
+            kvq.kvq_rabitq_encode_pack(cb, xs[j % P], ps[j % PO], ns[j % PO], 0, stream)
         out_bytes, norm_bytes, kname = nw * 4, 4, encode_kernel_name(D, 1, True, 0)
     else:
         sk = synth.tensor(synth.TensorSpec(1, 1, m, D, "gauss", 707), device=dev).reshape(m, D).contiguous()
         nw = m // 32
-        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(P)]
-        ns = [torch.empty((B, H, S), dtype=torch.float16, device=dev) for _ in range(P)]
+        PO = output_sets(P, n_vec * (nw * 4 + 2))
+        ps = [torch.empty((B, H, S, nw), dtype=torch.int32, device=dev) for _ in range(PO)]
+        ns = [torch.empty((B, H, S), dtype=torch.float16, device=dev) for _ in range(PO)]
 
         def enc(j):
-            kvq.kvq_qjl_encode_pack(sk, xs[j], ps[j], ns[j], 0, stream)
+            kvq.kvq_qjl_encode_pack(sk, xs[j % P], ps[j % PO], ns[j % PO], 0, stream)
         out_bytes, norm_bytes, kname = nw * 4, 2, f"kvq::qjl_encode_kernel<{D}, {m // 32}, true>"
 
     for i in range(args.warmup):
-        enc(i % P)
+        enc(i)
     torch.cuda.synchronize()
     K = args.steps
     e0, e1 = TimingEvent(), TimingEvent()
@@ -642,7 +657,7 @@ def bench_signcodes(args, idle: dict) -> int:
     prime(stream)
     e0.record(stream)
     for i in range(K):
-        enc((args.warmup + i) % P)
+        enc(args.warmup + i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -651,11 +666,11 @@ def bench_signcodes(args, idle: dict) -> int:
     gbps = alg / (us * 1e-6) / 1e9
 
     # parity re-check on a strided sample of the last timed output, and the oracle's time
-    j = (args.warmup + K - 1) % P
+    k = (args.warmup + K - 1) % PO
     idx = torch.arange(0, n_vec, max(1, n_vec // 65536))
-    rows = xs[j].reshape(-1, D)[idx.to(dev)].cpu().numpy()
-    dev_p = ps[j].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
-    dev_n = ns[j].reshape(-1)[idx.to(dev)].cpu().numpy()
+    rows = xs[k % P].reshape(-1, D)[idx.to(dev)].cpu().numpy()
+    dev_p = ps[k].reshape(-1, nw)[idx.to(dev)].cpu().numpy().view(np.uint32)
+    dev_n = ns[k].reshape(-1)[idx.to(dev)].cpu().numpy()
     t0 = time.perf_counter()
     if kind == "rabitq":
         ref = signcodes.rabitq_encode(rows, signs)
@@ -682,7 +697,7 @@ def bench_signcodes(args, idle: dict) -> int:
         "config": {"workload": f"{args.workload}: {w.note.split('; b=')[0]}; " + (
             "1-bit sign code of the rotated vector + fp32 norm" if kind == "rabitq"
             else f"1-bit sign sketch, m = {m} Gaussian rows (fp16) + fp16 norm"),
-            "shape": [B, H, S, D], "pool_tensors": P},
+            "shape": [B, H, S, D], "pool_tensors": P, "encode_output_sets": PO},
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(B * S / (us * 1e-6), 1), "encode_us_per_launch": round(us, 3),
         "norm_bytes_per_launch_not_counted": n_vec * norm_bytes, "wall_s_timed_region": round(wall, 4),
