@@ -98,18 +98,20 @@ __device__ __forceinline__ void quantize_run(const float (&y)[N], float K, float
       // Bucket tables: the code is base + [w > thr] of the entry that the bucket of
       // v = clamp(w + 1/2, 0, 1) selects (the clamp is the add's output modifier). The
       // entry's byte offset is read from the bits of v + 2^13 (spacing 2^-10: sixteen
-      // times the bucket count) and of v2 + 2^14 (spacing 2^-9, eight-byte entries).
+      // times the bucket count) and of v2 + 2^14 (spacing 2^-9, eight-byte entries). A code
+      // is below 2^BITS, so it is added to the shifted word rather than or-ed in: the
+      // comparison's carry then goes straight into the word (one shift, one add-with-carry).
       const float w1 = __builtin_fmaf(y[j], K, 0.0f);
       const float v1 = __builtin_amdgcn_fmed3f(w1 + 0.5f, 0.0f, 1.0f);
       const uint32_t o1 = __float_as_uint(v1 + 8192.0f) & 0x7F0u;
       const float4 e = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(t1s) + o1);
       const bool gt = w1 > e.x;
-      u1 = (u1 << BITS) | (__float_as_uint(e.y) + (gt ? 1u : 0u));
+      u1 = ((u1 << BITS) + __float_as_uint(e.y)) + (gt ? 1u : 0u);
       const float w2 = __builtin_fmaf(y[j], K2s, gt ? e.w : e.z);
       const float v2 = __builtin_amdgcn_fmed3f(w2 + 0.5f, 0.0f, 1.0f);
       const uint32_t o2 = __float_as_uint(v2 + 16384.0f) & 0x3F8u;
       const float2 e2 = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(t2s) + o2);
-      u2 = (u2 << BITS) | (__float_as_uint(e2.y) + (w2 > e2.x ? 1u : 0u));
+      u2 = ((u2 << BITS) + __float_as_uint(e2.y)) + (w2 > e2.x ? 1u : 0u);
     }
   }
   // Word fixups. Each field holds (P, low) with P = [value > 0] for stage 1 and
