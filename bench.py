@@ -177,10 +177,10 @@ def spread(per_block, block):
 
 def encode_kernel_name(D: int, bits: int, contig: bool, stages: int) -> str:
     """The encode kernel libkvq launches for this shape (the matrix-core kernel covers
-    D = 128, the butterfly kernel everything else)."""
+    D = 128 and, except at 3 bits, D = 256; the butterfly kernel everything else)."""
     c = "true" if contig else "false"
-    if D == 128:
-        return f"kvq::encode_mx_kernel<{bits}, {c}, {stages}>"
+    if D == 128 or (D == 256 and bits != 3):
+        return f"kvq::encode_mx_kernel<{D}, {bits}, {c}, {stages}>"
     return f"kvq::encode_kernel<{D}, {bits}, {c}, {stages}>"
 
 

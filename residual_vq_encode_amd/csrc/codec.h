@@ -11,13 +11,13 @@
 //
 // The pages' Metal kernel runs one threadgroup per vector and one thread per coordinate,
 // stages codes in threadgroup memory and packs them after a barrier. Here:
-//  * at D = 128 (encode_mx_kernel) a wave takes 16 vectors at a time and runs the transform
-//    on the matrix cores as H_4 (x) H_32: eight v_mfma_f32_16x16x32_f16 products of an
-//    fp16 +-1 H_32 slice with the sign-flipped fp16 inputs (exact products, float32 sums)
-//    and two float32 butterfly stages across the 32-coordinate blocks; each lane then
-//    quantizes 8 coordinates of every output block, and a 4 x 4 transpose of the code
-//    pieces across lane groups (v_permlane32_swap, v_permlane16_swap) gives each lane group
-//    a contiguous quarter of the vector's words;
+//  * at D = 128 and 256 (encode_mx_kernel; not 3 bits at 256) a wave takes 16 vectors at a
+//    time and runs the transform on the matrix cores as H_(D/32) (x) H_32: 2 D / 32
+//    v_mfma_f32_16x16x32_f16 products of an fp16 +-1 H_32 slice with the sign-flipped fp16
+//    inputs (exact products, float32 sums) and log2(D / 32) float32 butterfly stages across
+//    the 32-coordinate blocks; each lane then quantizes 8 coordinates of every output
+//    block, and 4 x 4 transposes of the code pieces across lane groups (v_permlane32_swap,
+//    v_permlane16_swap) give each lane group a contiguous quarter of the vector's words;
 //  * at every other D (encode_kernel) a vector of P coordinates (P = D, or the next power
 //    of two for other head dimensions) is spread over L = P / C lanes of a 64-wide
 //    wavefront, C = min(P, 32) consecutive coordinates per lane, and the Walsh-Hadamard
@@ -57,6 +57,13 @@ constexpr int kDecodeWavesPerEU = 4;
 template <int BITS, bool CONTIG>
 constexpr int encode_waves_per_eu() {
   return (!CONTIG && BITS >= 3) ? 3 : kEncodeWavesPerEU;
+}
+
+// The matrix-core encode at D = 256 holds twice the values per lane (64 transform outputs):
+// held to 128 registers it spilled, so it runs 3 waves per SIMD.
+template <int D>
+constexpr int mx_waves_per_eu() {
+  return D == 128 ? kEncodeWavesPerEU : 3;
 }
 
 // ------------------------------------------------------------------------------ quantizers
@@ -458,21 +465,22 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // length 8, i.e. the sign pattern of row r of the 8 x 8 Sylvester Hadamard matrix.
 constexpr uint64_t kWalsh8 = 0x963C5AF066CCAA00ull;
 
-// The encode of D = 128 with its transform on the matrix cores. The Sylvester matrix
-// factors as H_128 = H_4 (x) H_32: entry (32 g + r, 32 k + c) is (-1)^popcount(g & k) H_32[r][c].
-// So each 32-coordinate input block x_k of a vector is first transformed on its own,
-// z_k = H_32 x_k, and output block g is sum_k (-1)^popcount(g & k) z_k: two more butterfly
-// stages across the blocks. For a tile of 16 vectors the z_k are 8 products
-// v_mfma_f32_16x16x32_f16 (A = a 16 x 32 slice of H_32, B = input block k of the 16 vectors),
-// whose +-1 entries and fp16 inputs multiply exactly, summed in float32; the stages across
-// the blocks are float32 adds in registers. The rotation's signs diag(s) are applied to the
-// fp16 inputs first (an XOR of sign bits), as the butterfly kernel does through its weights.
+// The encodes of D = 128 and 256 with their transform on the matrix cores. The Sylvester
+// matrix factors as H_D = H_NB (x) H_32 (NB = D / 32 = 4 or 8): entry (32 g + r, 32 k + c) is
+// (-1)^popcount(g & k) H_32[r][c]. So each 32-coordinate input block x_k of a vector is first
+// transformed on its own, z_k = H_32 x_k, and output block g is sum_k (-1)^popcount(g & k) z_k:
+// log2(NB) more butterfly stages across the blocks. For a tile of 16 vectors the z_k are 2 NB
+// products v_mfma_f32_16x16x32_f16 (A = a 16 x 32 slice of H_32, B = input block k of the 16
+// vectors), whose +-1 entries and fp16 inputs multiply exactly, summed in float32; the stages
+// across the blocks are float32 adds in registers. The rotation's signs diag(s) are applied
+// to the fp16 inputs first (an XOR of sign bits), as the butterfly kernel does through its
+// weights.
 //
 // Why the matrix cores: the butterfly kernel spends about 6.5 VALU instructions per
 // coordinate on the transform, as many as its quantizers and packing together, and a wave's
-// last tile is computed after the input stream has ended; here the transform is 8 MFMAs and
-// 64 adds per 16-vector tile, about 280 VALU instructions in all against 450, which shortens
-// both the arithmetic that the memory stream has to hide and that tail.
+// last tile is computed after the input stream has ended; here (D = 128) the transform is 8
+// MFMAs and 64 adds per 16-vector tile, about 280 VALU instructions in all against 450,
+// which shortens both the arithmetic that the memory stream has to hide and that tail.
 //
 // MFMA layout (16x16x32): lane l supplies row l % 16 of A and column l % 16 of B, each with
 // the 8 k-values 8 (l / 16) + [0, 8), and receives D[4 (l / 16) + i][l % 16], i < 4. B's
@@ -482,18 +490,19 @@ constexpr uint64_t kWalsh8 = 0x963C5AF066CCAA00ull;
 // carries H_32 row 8 (m >> 2) + 4 mh + (m & 3), so that lane group g receives the block
 // coordinates 8 g + 4 mh + i: over the two halves, 8 consecutive coordinates of every block,
 // and of every output block after the stages across blocks. Their codes are 8 consecutive
-// fields of one packed word (BITS = 4) or a quarter or half of one (BITS = 1, 2); a 4 x 4
-// transpose of those pieces across the four lane groups (v_permlane32_swap, then
-// v_permlane16_swap) leaves lane group g with the vector's words [g NW / 4, (g + 1) NW / 4),
-// stored as one contiguous run. At BITS = 3 a piece is 24 bits and the transpose leaves lane
+// fields of one packed word (BITS = 4) or a quarter or half of one (BITS = 1, 2); NB / 4
+// transposes of those pieces across the four lane groups (v_permlane32_swap, then
+// v_permlane16_swap), each over blocks NB / 4 apart, leave lane group g with output blocks
+// [g NB / 4, (g + 1) NB / 4), i.e. the vector's words [g NW / 4, (g + 1) NW / 4), stored as
+// one contiguous run. At BITS = 3 (D = 128) a piece is 24 bits and the transpose leaves lane
 // group g with the 96-bit slice of the code stream that holds codes [32 g, 32 g + 32); the
 // 30-bit words (10 codes and 2 spare bits each) are cut from the slices as in the butterfly
 // kernel, and a contiguous cache receives each tile's 208 words per stream through LDS as
 // one run of 16-byte stores.
-template <int BITS, bool CONTIG, int STAGES>
-__global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_kernel(const EncodeArgs a) {
-  constexpr int D = 128;
+template <int D, int BITS, bool CONTIG, int STAGES>
+__global__ __launch_bounds__(kBlockThreads, (mx_waves_per_eu<D>())) void encode_mx_kernel(const EncodeArgs a) {
   constexpr int NB = D / 32;             // 32-coordinate blocks of a vector
+  constexpr int BPG = NB / 4;            // output blocks each lane group stores
   constexpr int CPV = D / 8;             // 16-byte chunks per vector
   constexpr int TV = kMxTile;            // vectors per tile: the MFMA's 16 columns
   constexpr int TCH = TV * CPV;          // chunks per tile
@@ -501,16 +510,27 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
   constexpr int NW = (D + EPW - 1) / EPW;  // words per vector per stream
   constexpr bool B3 = BITS == 3;         // 10-code words straddle the lane groups' slices
   constexpr int WPL = B3 ? 4 : NW / 4;   // words each lane group holds per stream (B3: 3 or 4)
+  constexpr int WB = B3 ? 0 : NW / NB;   // words of one 32-coordinate block per stream
   constexpr bool TWO = STAGES == 2;
   constexpr int NSTREAM = TWO ? 2 : 1;
   constexpr int TW = TV * NW;            // words of a tile per stream
   constexpr bool RUN = B3 && CONTIG;     // B3 words to a contiguous cache: one run through LDS
-  static_assert(TV == 16 && NB == 4, "16 vectors of 4 blocks: one MFMA column per vector, one lane group per block");
+  constexpr bool MASKS_LDS = NB > 4;     // the sign masks of 8 blocks would hold 32 registers
+  static_assert(TV == 16 && (NB == 4 || NB == 8), "16 vectors of 4 or 8 blocks: one MFMA column per vector");
+  static_assert(!B3 || NB == 4, "3-bit slices: 4 blocks, one per lane group");
   static_assert(STAGES != 0 || BITS == 1, "the sign code is one bit per coordinate");
   static_assert(!RUN || (TW % 4 == 0 && TW / 4 <= 64), "a tile's run is at most one 16-byte chunk per lane");
 
   __shared__ u32x4_t stage[kWavesPerBlock][TCH];
   __shared__ uint32_t pk[RUN ? kWavesPerBlock : 1][RUN ? NSTREAM * TW : 1];
+  // MASKS_LDS: the sign-bit masks of diag(s) for chunk 4 k + g of every vector, at [4 k + g]
+  __shared__ u32x4_t smask[MASKS_LDS ? 4 * NB : 1];
+  if constexpr (MASKS_LDS) {
+    for (int i = threadIdx.x; i < 4 * NB; i += kBlockThreads)
+      smask[i] = u32x4_t{a.wpair[4 * i] ^ kOnePair, a.wpair[4 * i + 1] ^ kOnePair, a.wpair[4 * i + 2] ^ kOnePair,
+                         a.wpair[4 * i + 3] ^ kOnePair};
+    if constexpr (BITS < 3) __syncthreads();
+  }
   constexpr int TSLOTS = BITS >= 3 ? 128 : 1;
   __shared__ float4 t1s[TSLOTS];
   __shared__ float2 t2s[TSLOTS];
@@ -562,11 +582,13 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
   // diag(s) over this lane's input chunks 4 k + g, and the A operands of the two output
   // halves (row m = v: H_32 row 8 (v >> 2) + 4 mh + (v & 3) at columns 8 g + t, t < 8, as
   // fp16 +-1 pairs).
-  u32x4_t mk[NB];
+  u32x4_t mk[MASKS_LDS ? 1 : NB];
+  if constexpr (!MASKS_LDS) {
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
+    for (int k = 0; k < NB; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mk[k][i] = a.wpair[4 * (4 * k + g) + i] ^ kOnePair;
+      for (int i = 0; i < 4; ++i) mk[k][i] = a.wpair[4 * (4 * k + g) + i] ^ kOnePair;
+  }
   f16x8_t ah[2];
 #pragma unroll
   for (int mh = 0; mh < 2; ++mh) {
@@ -649,10 +671,10 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
     if (tile + stride < n_tiles) dma(tile + stride);
 
     // 3. diag(s) on the fp16 inputs, the blocks' transforms z_k (register i of half mh is
-    //    block coordinate 8 g + 4 mh + i), then the two stages across the blocks: output block
-    //    gb = sum_k (-1)^popcount(gb & k) z_k.
+    //    block coordinate 8 g + 4 mh + i), then the log2(NB) stages across the blocks: output
+    //    block gb = sum_k (-1)^popcount(gb & k) z_k.
     f32x4_t y4[NB][2];
-    {
+    if constexpr (NB == 4) {
       f32x4_t z[NB][2];
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
@@ -670,6 +692,34 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
           y4[1][mh][i] = d0 + d1;
           y4[2][mh][i] = s0 - s1;
           y4[3][mh][i] = d0 - d1;
+        }
+    } else {
+      f32x4_t z[NB][2];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const f16x8_t bx = __builtin_bit_cast(f16x8_t, bq[k] ^ smask[4 * k + g]);
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh) z[k][mh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mh], bx, f32x4_t{}, 0, 0, 0);
+      }
+      // element by element: all the stages of one (mh, i) before the next
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float t[NB];
+#pragma unroll
+          for (int k = 0; k < NB; ++k) t[k] = z[k][mh][i];
+#pragma unroll
+          for (int h = 1; h < NB; h *= 2)
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+              if ((k & h) == 0) {
+                const float p = t[k], q = t[k + h];
+                t[k] = p + q;
+                t[k + h] = p - q;
+              }
+#pragma unroll
+          for (int k = 0; k < NB; ++k) y4[k][mh][i] = t[k];
         }
     }
 
@@ -718,48 +768,51 @@ __global__ __launch_bounds__(kBlockThreads, kEncodeWavesPerEU) void encode_mx_ke
       quantize_run<BITS, STAGES, 0, 8>(y, K, K2, K2s, a, t1s, t2s, pc1[gb], pc2[gb]);
     }
 
-    // 6. Transpose the pieces across the lane groups: piece gb of group g' goes to group gb,
-    //    slot g' (two swaps across lane halves, then two across 16-lane rows), so group g
-    //    holds the pieces of output block g from groups 0..3 in order, i.e. the vector's
-    //    words [g WPL, g WPL + WPL) once joined.
+    // 6. Transpose the pieces across the lane groups, BPG times: in round r, piece
+    //    BPG j + r of group g' goes to group j, slot g' (two swaps across lane halves, then
+    //    two across 16-lane rows), so group g holds the pieces of output blocks BPG g + r
+    //    from groups 0..3 in order, i.e. the vector's words [g WPL, g WPL + WPL) once joined.
     auto gather = [&](const uint32_t (&pc)[NB], uint32_t (&o)[WPL]) {
-      uint32_t w[4] = {pc[0], pc[1], pc[2], pc[3]};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(w[j], w[j + 2], false, false);
-        w[j] = sw[0];
-        w[j + 2] = sw[1];
-      }
+      for (int r = 0; r < BPG; ++r) {
+        uint32_t w[4] = {pc[r], pc[BPG + r], pc[2 * BPG + r], pc[3 * BPG + r]};
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(w[j], w[j + 1], false, false);
-        w[j] = sw[0];
-        w[j + 1] = sw[1];
-      }
-      if constexpr (BITS == 4) {
+        for (int j = 0; j < 2; ++j) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(w[j], w[j + 2], false, false);
+          w[j] = sw[0];
+          w[j + 2] = sw[1];
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = w[j];
-      } else if constexpr (BITS == 3) {
-        // the 96-bit slice as three dwords, then the 30-bit words starting in it (the last
-        // one reads on into the next group's slice; zero past the vector's end)
-        const uint32_t d0 = w[0] | (w[1] << 24);
-        const uint32_t d1 = (w[1] >> 8) | (w[2] << 16);
-        const uint32_t d2 = (w[2] >> 16) | (w[3] << 8);
-        uint32_t nb = static_cast<uint32_t>(__shfl(static_cast<int>(d0), lane + 16));
-        if (g == NB - 1) nb = 0u;
-        constexpr uint32_t M30 = 0x3FFFFFFFu;
-        const uint32_t at0 = s_off == 0 ? 0xFFFFFFFFu : 0u;  // a bit-select, not a branch
-        o[0] = __builtin_amdgcn_alignbit(d1, d0, s_off) & M30;
-        o[1] = ((__builtin_amdgcn_alignbit(d1, d0, 30) & at0) |
-                (__builtin_amdgcn_alignbit(d2, d1, s_off - 2) & ~at0)) & M30;
-        o[2] = ((__builtin_amdgcn_alignbit(d2, d1, 28) & at0) |
-                (__builtin_amdgcn_alignbit(nb, d2, s_off - 4) & ~at0)) & M30;
-        o[3] = __builtin_amdgcn_alignbit(nb, d2, 26) & M30;  // stored only when s_off == 0
-      } else if constexpr (BITS == 2) {
-        o[0] = w[0] | (w[1] << 16);
-        o[1] = w[2] | (w[3] << 16);
-      } else {
-        o[0] = w[0] | (w[1] << 8) | (w[2] << 16) | (w[3] << 24);
+        for (int j = 0; j < 4; j += 2) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(w[j], w[j + 1], false, false);
+          w[j] = sw[0];
+          w[j + 1] = sw[1];
+        }
+        if constexpr (BITS == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[WB * r + j] = w[j];
+        } else if constexpr (BITS == 3) {
+          // the 96-bit slice as three dwords, then the 30-bit words starting in it (the last
+          // one reads on into the next group's slice; zero past the vector's end)
+          const uint32_t d0 = w[0] | (w[1] << 24);
+          const uint32_t d1 = (w[1] >> 8) | (w[2] << 16);
+          const uint32_t d2 = (w[2] >> 16) | (w[3] << 8);
+          uint32_t nb = static_cast<uint32_t>(__shfl(static_cast<int>(d0), lane + 16));
+          if (g == NB - 1) nb = 0u;
+          constexpr uint32_t M30 = 0x3FFFFFFFu;
+          const uint32_t at0 = s_off == 0 ? 0xFFFFFFFFu : 0u;  // a bit-select, not a branch
+          o[0] = __builtin_amdgcn_alignbit(d1, d0, s_off) & M30;
+          o[1] = ((__builtin_amdgcn_alignbit(d1, d0, 30) & at0) |
+                  (__builtin_amdgcn_alignbit(d2, d1, s_off - 2) & ~at0)) & M30;
+          o[2] = ((__builtin_amdgcn_alignbit(d2, d1, 28) & at0) |
+                  (__builtin_amdgcn_alignbit(nb, d2, s_off - 4) & ~at0)) & M30;
+          o[3] = __builtin_amdgcn_alignbit(nb, d2, 26) & M30;  // stored only when s_off == 0
+        } else if constexpr (BITS == 2) {
+          o[WB * r] = w[0] | (w[1] << 16);
+          o[WB * r + 1] = w[2] | (w[3] << 16);
+        } else {
+          o[WB * r] = w[0] | (w[1] << 8) | (w[2] << 16) | (w[3] << 24);
+        }
       }
     };
     gather(pc1, o1);
@@ -1023,8 +1076,8 @@ static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   static int cap[2][2] = {{0, 0}, {0, 0}};
   const bool c = a.map.contiguous != 0;
   if constexpr (encode_on_matrix_cores(D, BITS) && ROWS == kRowsFull) {
-    const void* f = c ? reinterpret_cast<const void*>(&encode_mx_kernel<BITS, true, STAGES>)
-                      : reinterpret_cast<const void*>(&encode_mx_kernel<BITS, false, STAGES>);
+    const void* f = c ? reinterpret_cast<const void*>(&encode_mx_kernel<D, BITS, true, STAGES>)
+                      : reinterpret_cast<const void*>(&encode_mx_kernel<D, BITS, false, STAGES>);
     return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, kMxTile, cap[c ? 1 : 0], true, stream);
   } else {
     const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES, ROWS>)

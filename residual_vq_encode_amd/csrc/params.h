@@ -49,9 +49,12 @@ constexpr int row_mode(int d) {
   return d == rotation_length(d) ? kRowsFull : (d % 8 == 0 ? kRowsChunks : kRowsRagged);
 }
 
-// The encode of D = 128 runs its transform on the matrix cores (every bit width); every
-// other shape (padded ones included) takes the butterfly kernel.
-constexpr bool encode_on_matrix_cores(int d, int bits) { return d == 128 && bits >= 1; }
+// The encodes of D = 128 (every bit width) and D = 256 (1, 2 and 4 bits) run their
+// transform on the matrix cores; every other shape (padded ones included) takes the
+// butterfly kernel.
+constexpr bool encode_on_matrix_cores(int d, int bits) {
+  return (d == 128 && bits >= 1) || (d == 256 && bits >= 1 && bits != 3);
+}
 
 // Vectors per wave tile (the unit of work of the persistent grids, indexed with 32-bit
 // integers): the matrix-core encode takes 16; the butterfly kernels spread a vector over

@@ -391,7 +391,8 @@ void test_tampered_codebooks() {
 
 // The kernels index their tiles with 32-bit integers: a launch needing more than INT_MAX
 // tiles is refused with KVQ_ERR_RANGE on the host (at d = 1024 the butterfly kernels hold 2
-// vectors per tile; at d = 128 the matrix-core encode and the decode hold 16).
+// vectors per tile, at d = 256 8; the matrix-core encodes at d = 128 and 256 and the decode
+// at d = 128 hold 16).
 void test_tile_limit() {
   uint16_t* x = fake<uint16_t>(0x10000);
   uint32_t* p1 = fake<uint32_t>(0x20000);
@@ -410,6 +411,12 @@ void test_tile_limit() {
   CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax, p1, p2, nr, 16 * imax, 0, nullptr) == KVQ_OK);
   CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax + 1, p1, p2, nr, 16 * imax + 1, 0, nullptr) == KVQ_ERR_RANGE);
   CHECK(kvq_rvq_unpack_decode(&cb, p1, p2, nr, 1, 1, 16 * imax + 1, 0, 16 * imax + 1, x, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_build_codebooks(256, 2, nullptr, &cb) == KVQ_OK);  // matrix cores
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax, p1, p2, nr, 16 * imax, 0, nullptr) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 16 * imax + 1, p1, p2, nr, 16 * imax + 1, 0, nullptr) == KVQ_ERR_RANGE);
+  CHECK(kvq_build_codebooks(256, 3, nullptr, &cb) == KVQ_OK);  // butterfly
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 8 * imax, p1, p2, nr, 8 * imax, 0, nullptr) == KVQ_OK);
+  CHECK(kvq_rvq_encode_pack(&cb, x, 1, 1, 8 * imax + 1, p1, p2, nr, 8 * imax + 1, 0, nullptr) == KVQ_ERR_RANGE);
 }
 
 // The allocation-free attention: the same checks as kvq_rvq_attend, all on the host before

@@ -27,8 +27,10 @@ def test_block_size_leaves_four_blocks_at_short_runs():
 
 
 def test_encode_kernel_names():
-    assert bench.encode_kernel_name(128, 2, True, 2) == "kvq::encode_mx_kernel<2, true, 2>"
-    assert bench.encode_kernel_name(128, 3, True, 2) == "kvq::encode_mx_kernel<3, true, 2>"
+    assert bench.encode_kernel_name(128, 2, True, 2) == "kvq::encode_mx_kernel<128, 2, true, 2>"
+    assert bench.encode_kernel_name(128, 3, True, 2) == "kvq::encode_mx_kernel<128, 3, true, 2>"
+    assert bench.encode_kernel_name(256, 4, True, 2) == "kvq::encode_mx_kernel<256, 4, true, 2>"
+    assert bench.encode_kernel_name(256, 3, True, 2) == "kvq::encode_kernel<256, 3, true, 2>"
     assert bench.encode_kernel_name(64, 2, False, 1) == "kvq::encode_kernel<64, 2, false, 1>"
 
 
