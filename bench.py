@@ -499,36 +499,52 @@ def main() -> int:
         enc(i)
     torch.cuda.synchronize()
 
-    # The K steps' encodes run first, then their decodes, each in blocks of back-to-back
-    # launches with events between the blocks (per-block averages give the spread and an A/A
-    # noise floor from alternate blocks). Grouping the kernels keeps each in its own steady
-    # state: a decode block writes ten 67 MB outputs, and encodes interleaved with it would
-    # share the HBM with the write-back of those bytes.
+    # The K steps' encodes run first, then their decodes, all back to back, with one event
+    # before the encodes, one between the two phases and one after the decodes: an event
+    # between launches leaves a gap in the stream (about 0.4 us per launch with one every 5
+    # launches), so the timed region holds none. Grouping the kernels keeps each in its own
+    # steady state: a decode writes a 67 MB output, and encodes interleaved with the decodes
+    # would share the HBM with the write-back of those bytes.
     K = args.steps
-    BLOCK = block_size(K)
-    blocks = [(a, min(a + BLOCK, K)) for a in range(0, K, BLOCK)]
-    nb = len(blocks)
-    ev = [TimingEvent() for _ in range(2 * nb + 1)]
+    ev = [TimingEvent() for _ in range(3)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     prime(stream)
     ev[0].record(stream)
-    for bi, (a, b) in enumerate(blocks):
-        for i in range(a, b):
-            enc(args.warmup + i)
-        ev[bi + 1].record(stream)
-    for bi, (a, b) in enumerate(blocks):
-        for i in range(a, b):
-            dec(args.warmup + i)
-        ev[nb + bi + 1].record(stream)
+    for i in range(K):
+        enc(args.warmup + i)
+    ev[1].record(stream)
+    for i in range(K):
+        dec(args.warmup + i)
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    enc_us = ev[0].elapsed_time(ev[1]) * 1e3 / K
+    dec_us = ev[1].elapsed_time(ev[2]) * 1e3 / K
+    total_ms = ev[0].elapsed_time(ev[2])
 
-    enc_blk = [ev[bi].elapsed_time(ev[bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
-    dec_blk = [ev[nb + bi].elapsed_time(ev[nb + bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
-    enc_us = sum(t * (b - a) for t, (a, b) in zip(enc_blk, blocks)) / K
-    dec_us = sum(t * (b - a) for t, (a, b) in zip(dec_blk, blocks)) / K
-    total_ms = ev[0].elapsed_time(ev[-1])
+    # Spread pass, after the timed region and not part of its figures: K more encodes, then K
+    # more decodes, in blocks with an event after each block. The per-block averages give
+    # p10 / p50 / p90 and the A/A noise floor (alternate blocks).
+    BLOCK = block_size(K)
+    blocks = [(a, min(a + BLOCK, K)) for a in range(0, K, BLOCK)]
+    nb = len(blocks)
+    evs = [TimingEvent() for _ in range(2 * nb + 1)]
+    torch.cuda.synchronize()
+    prime(stream)
+    evs[0].record(stream)
+    for bi, (a, b) in enumerate(blocks):
+        for i in range(a, b):
+            enc(args.warmup + K + i)
+        evs[bi + 1].record(stream)
+    for bi, (a, b) in enumerate(blocks):
+        for i in range(a, b):
+            dec(args.warmup + K + i)
+        evs[nb + bi + 1].record(stream)
+    torch.cuda.synchronize()
+    enc_blk = [evs[bi].elapsed_time(evs[bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+    dec_blk = [evs[nb + bi].elapsed_time(evs[nb + bi + 1]) * 1e3 / (b - a) for bi, (a, b) in enumerate(blocks)]
+
     n_vec = B * H * S
     enc_bytes = n_vec * (D * 2 + stages * nw * 4)
     dec_bytes = n_vec * (stages * nw * 4 + 4 + D * 2)
@@ -581,6 +597,8 @@ def main() -> int:
         "head_vectors_per_s": round(n_vec / (enc_us * 1e-6), 1),
         "encode_us_per_launch": round(enc_us, 3),
         "encode_us_blocks": spread(enc_blk, BLOCK),
+        "spread_pass": "the blocks' figures come from K more launches after the timed region, "
+                       "with an event after each block; value and the per-launch times do not use them",
         "decode_us_per_launch": round(dec_us, 3),
         "decode_us_blocks": spread(dec_blk, BLOCK),
         "decode_GBps": round(dec_gbps, 1),
