@@ -1042,8 +1042,10 @@ static bool residency(const void* f, int* cus, int* per_cu) {
 // fewest waves on one SIMD (a block's waves sit on the four SIMDs of its CU), preferring
 // more blocks on ties: the matrix-core encode's 16384 tiles on 256 CUs run as 3 blocks per
 // CU (5 rounds of 3072 waves and a last round of 1024, one wave per SIMD) rather than 4
-// (4 full rounds). The decodes keep every resident block: their last round is short and
-// the writes of the others' tiles hide it.
+// (4 full rounds). The decodes and the 3- and 4-bit matrix-core encodes keep every resident
+// block: a decode's last round is short and the writes of the others' tiles hide it, and
+// the 3- and 4-bit encodes are held by their arithmetic, which more waves in flight
+// overlap better (4 blocks per CU: 3.5 % faster at 3 bits, the same at 4).
 static hipError_t launch(const void* f, void* args, int64_t n_vec, int vw, int* cap, bool balance,
                          hipStream_t stream) {
   const int64_t tiles = (n_vec + vw - 1) / vw;
@@ -1078,7 +1080,7 @@ static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   if constexpr (encode_on_matrix_cores(D, BITS) && ROWS == kRowsFull) {
     const void* f = c ? reinterpret_cast<const void*>(&encode_mx_kernel<D, BITS, true, STAGES>)
                       : reinterpret_cast<const void*>(&encode_mx_kernel<D, BITS, false, STAGES>);
-    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, kMxTile, cap[c ? 1 : 0], true, stream);
+    return launch(f, const_cast<EncodeArgs*>(&a), a.n_vec, kMxTile, cap[c ? 1 : 0], BITS < 3, stream);
   } else {
     const void* f = c ? reinterpret_cast<const void*>(&encode_kernel<D, BITS, true, STAGES, ROWS>)
                       : reinterpret_cast<const void*>(&encode_kernel<D, BITS, false, STAGES, ROWS>);
