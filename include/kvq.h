@@ -34,7 +34,9 @@ typedef enum kvq_status {
   KVQ_ERR_ARG = -1,    /* a required pointer is NULL, or a codebook struct is inconsistent */
   KVQ_ERR_SHAPE = -2,  /* d outside [8, 1024] (or not a power of two where stated); bits not in 1..4; B, H, S < 0 */
   KVQ_ERR_ALIGN = -3,  /* an fp16 or packed-word buffer not 16-byte aligned, or a norm buffer not 4-byte aligned */
-  KVQ_ERR_RANGE = -4,  /* s_offset < 0, s_offset + S > S_cap, or a size overflows 64 bits */
+  KVQ_ERR_RANGE = -4,  /* s_offset < 0, s_offset + S > S_cap, a size overflows 64 bits, or a
+                          launch would need more than 2^31 - 1 tiles (the kernels index tiles
+                          with 32-bit integers; a tile is 2 to 64 vectors, by kernel and d) */
   KVQ_ERR_DEVICE = -5  /* the HIP launch reported an error */
 } kvq_status;
 
